@@ -1,0 +1,59 @@
+"""Work and traffic model for the quantized-GEMM path, and MI355X peaks.
+
+The model follows the page "JAX Pallas 在 TPU 上编写高效矩阵乘法内核" (JAX Pallas
+matmul kernels on TPU), section "矩阵乘法性能分析 / FLOPs 与内存带宽": a matmul
+costs 2*m*k*n operations, and its minimum memory traffic is every input read
+once plus the output written once.  With mixed operand widths each operand is
+counted at its own width (B at bits/8 bytes per element, fp16 scale and
+output at 2 bytes, int32 output at 4).  These are ALGORITHMIC quantities: the
+re-reads a tiled kernel makes are not counted here (they show up in the
+hardware counters instead).
+"""
+from __future__ import annotations
+
+# MI355X published peaks (dense, no sparsity).
+HBM_PEAK_BYTES_PER_S = 8.0e12
+INT8_MFMA_PEAK_OPS_PER_S = 5.0e15
+FP32_VECTOR_PEAK_FLOPS = 157.3e12
+
+
+def matmul_flops(m: int, k: int, n: int) -> int:
+    """2*m*k*n, as on the Pallas page."""
+    return 2 * m * k * n
+
+
+def matmul_membw(m: int, k: int, n: int, itemsize: int) -> int:
+    """(m*k + k*n + m*n) * itemsize bytes, as on the Pallas page."""
+    return (m * k + k * n + m * n) * itemsize
+
+
+def gemm_ops(M: int, N: int, K: int) -> int:
+    return matmul_flops(M, K, N)
+
+
+def gemm_bytes(M: int, N: int, K: int, bits: int, out: str = "f16") -> int:
+    """A int8 [M,K] + B at `bits` [N,K] + fp16 scale [N] (f16 output only)
+    + output [M,N] (fp16 or int32)."""
+    b = M * K + (N * K * bits) // 8
+    if out == "f16":
+        b += 2 * N + 2 * M * N
+    else:
+        b += 4 * M * N
+    return b
+
+
+def quantize_bytes(rows: int, cols: int) -> int:
+    """fp16 x read once, int8 codes and fp16 scales written once."""
+    return rows * cols * 2 + rows * cols + rows * 2
+
+
+def pack_bytes(n: int, k: int, bits: int) -> int:
+    """int8 values read once, packed bytes written once."""
+    return n * k + (n * k * bits) // 8
+
+
+def bound(ops: float, nbytes: float):
+    """Which roofline bounds a kernel with this work: ('hbm'|'mfma', seconds)."""
+    t_mem = nbytes / HBM_PEAK_BYTES_PER_S
+    t_ops = ops / INT8_MFMA_PEAK_OPS_PER_S
+    return ("hbm", t_mem) if t_mem >= t_ops else ("mfma", t_ops)
