@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-GEMM hot path on one MI355X.
+
+One step is one pass of every kernel of the path over one batch of
+synthetic, HBM-resident inputs, in the order a model would run them:
+
+  1. quantize_rows   fp16 fused-QKV weight [12288, 4096] -> int8 codes + fp16 scales
+  2. gemm w8a8       those codes, M = 64 (streaming path, chosen by M)
+  3. pack_int4       int4 weight values [4096, 4096] -> [4096, 2048] bytes
+  4. gemm w4a8       decode GEMV, M = 1, N = K = 4096 (streaming path)
+  5. gemm w4a8       prefill, M = 4096, N = K = 4096 (tiled matrix-core path)
+  6. pack_int2       ternary weight values [4096, 4096] -> [4096, 1024] bytes
+  7. gemm w2a8       ternary, M = 1 and M = 128, N = K = 4096
+
+Memory-bound steps read their inputs from rings of distinct buffers larger
+than twice the 256 MB Infinity Cache, so every timed read comes from HBM.
+Each kernel is timed with HIP events recorded on the stream it runs on;
+`value` is the headline: int8 TOPS of the M = 4096 W4A8 GEMM.  The decode
+GEMV's HBM GB/s and every other kernel's rate are reported under "kernels".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized GEMM TOPS (M=4096) + GEMV HBM GB/s (M=1), % of MI355X roofline"
+MALL_BYTES = 256 << 20
+HOLD_CYCLES = 50_000_000
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def ring_len(nbytes: int, minimum: int = 2) -> int:
+    """Copies needed so that a ring of buffers spans > 2x the MALL."""
+    return max(minimum, -(-2 * MALL_BYTES // max(nbytes, 1)) + 1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU kernels "
+              "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_mixed_precision_amd import bq, roofline, synth
+
+    if not os.path.exists(bq.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.float16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def ring(t, n):
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    # ---------------- inputs (host draws, uploaded once) ----------------
+    K = 4096
+    W, A64 = synth.bminf_case(M=64, rows=3 * 4096, cols=K, seed=0)
+    A4096, B4v, s4 = synth.w4a8_case(4096, 4096, K, seed=0)
+    A1 = A4096[:1].copy()
+    A2, B2v, s2 = synth.w2a8_case(128, 4096, K, seed=0)
+    A2_1 = A2[:1].copy()
+
+    W_d = ring(up(W), ring_len(W.nbytes))
+    A64_d = up(A64)
+    q_ring = [torch.empty(W.shape, dtype=torch.int8, device=dev) for _ in range(ring_len(W.size))]
+    s_ring = [torch.empty(W.shape[0], dtype=torch.float16, device=dev) for _ in q_ring]
+    B4v_d = ring(up(B4v), ring_len(B4v.nbytes))
+    B4p_ring = [torch.empty((4096, K // 2), dtype=torch.uint8, device=dev)
+                for _ in range(ring_len(4096 * K // 2))]
+    B2v_d = ring(up(B2v), ring_len(B2v.nbytes))
+    B2p_ring = [torch.empty((4096, K // 4), dtype=torch.uint8, device=dev)
+                for _ in range(ring_len(4096 * K // 4))]
+    s4_d, s2_d = up(s4), up(s2)
+    A4096_d, A1_d, A2_d, A2_1_d = up(A4096), up(A1), up(A2), up(A2_1)
+    C64 = torch.empty((64, W.shape[0]), dtype=torch.float16, device=dev)
+    C1 = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+    C4096 = torch.empty((4096, 4096), dtype=torch.float16, device=dev)
+    C2_1 = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+    C2_128 = torch.empty((128, 4096), dtype=torch.float16, device=dev)
+
+    # fill every ring slot once (packed weights and codes) before timing
+    for i in range(len(q_ring)):
+        bq.quantize_rows(W_d[i % len(W_d)], q_ring[i], s_ring[i])
+    for i in range(len(B4p_ring)):
+        bq.pack_int4(B4v_d[i % len(B4v_d)], B4p_ring[i])
+    for i in range(len(B2p_ring)):
+        bq.pack_int2(B2v_d[i % len(B2v_d)], B2p_ring[i])
+    torch.cuda.synchronize()
+
+    # ---------------- the step ----------------
+    names = ["quantize_rows", "gemm_w8a8_m64", "pack_int4", "gemm_w4a8_m1",
+             "gemm_w4a8_m4096", "pack_int2", "gemm_w2a8_m1", "gemm_w2a8_m128"]
+
+    def step(i, ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+        mark(0)
+        qi = i % len(q_ring)
+        bq.quantize_rows(W_d[i % len(W_d)], q_ring[qi], s_ring[qi])
+        mark(1)
+        qj = (i + len(q_ring) // 2) % len(q_ring)  # codes written a while ago
+        bq.gemm_w8a8_dequant(A64_d, q_ring[qj], s_ring[qj], C64)
+        mark(2)
+        pi = i % len(B4p_ring)
+        bq.pack_int4(B4v_d[i % len(B4v_d)], B4p_ring[pi])
+        mark(3)
+        pj = (i + len(B4p_ring) // 2) % len(B4p_ring)
+        bq.gemm_w4a8_dequant(A1_d, B4p_ring[pj], s4_d, C1)
+        mark(4)
+        bq.gemm_w4a8_dequant(A4096_d, B4p_ring[pj], s4_d, C4096)
+        mark(5)
+        ri = i % len(B2p_ring)
+        bq.pack_int2(B2v_d[i % len(B2v_d)], B2p_ring[ri])
+        mark(6)
+        rj = (i + len(B2p_ring) // 2) % len(B2p_ring)
+        bq.gemm_w2a8_dequant(A2_1_d, B2p_ring[rj], s2_d, C2_1)
+        mark(7)
+        bq.gemm_w2a8_dequant(A2_d, B2p_ring[rj], s2_d, C2_128)
+        mark(8)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def hold_gpu():
+        # A device-side spin ahead of the timed work lets the host enqueue the
+        # whole timed region before the GPU reaches it, so host launch
+        # overhead never leaves the GPU idle between timed kernels.
+        try:
+            torch.cuda._sleep(HOLD_CYCLES)
+            return True
+        except Exception:
+            return False
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    held = hold_gpu()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dur_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(names))]
+                       for i in range(args.steps)])
+    mean_ms = dur_ms.mean(axis=0)
+    gpu_ms_per_step = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
+
+    # Sustained decode GEMV: back-to-back launches over the ring of packed
+    # weights (each launch reads a different 8 MiB buffer from HBM).
+    reps = 4 * len(B4p_ring)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    hold_gpu()
+    g0.record()
+    for r in range(reps):
+        bq.gemm_w4a8_dequant(A1_d, B4p_ring[r % len(B4p_ring)], s4_d, C1)
+    g1.record()
+    torch.cuda.synchronize()
+    gemv_sustained_us = g0.elapsed_time(g1) * 1e3 / reps
+
+    # ---------------- algorithmic work per kernel ----------------
+    work = {
+        "quantize_rows": dict(shape=[12288, 4096], bytes=roofline.quantize_bytes(12288, 4096), ops=0),
+        "gemm_w8a8_m64": dict(shape=[64, 12288, 4096], bytes=roofline.gemm_bytes(64, 12288, K, 8),
+                              ops=roofline.gemm_ops(64, 12288, K)),
+        "pack_int4": dict(shape=[4096, 4096], bytes=roofline.pack_bytes(4096, K, 4), ops=0),
+        "gemm_w4a8_m1": dict(shape=[1, 4096, 4096], bytes=roofline.gemm_bytes(1, 4096, K, 4),
+                             ops=roofline.gemm_ops(1, 4096, K)),
+        "gemm_w4a8_m4096": dict(shape=[4096, 4096, 4096], bytes=roofline.gemm_bytes(4096, 4096, K, 4),
+                                ops=roofline.gemm_ops(4096, 4096, K)),
+        "pack_int2": dict(shape=[4096, 4096], bytes=roofline.pack_bytes(4096, K, 2), ops=0),
+        "gemm_w2a8_m1": dict(shape=[1, 4096, 4096], bytes=roofline.gemm_bytes(1, 4096, K, 2),
+                             ops=roofline.gemm_ops(1, 4096, K)),
+        "gemm_w2a8_m128": dict(shape=[128, 4096, 4096], bytes=roofline.gemm_bytes(128, 4096, K, 2),
+                               ops=roofline.gemm_ops(128, 4096, K)),
+    }
+    kernels = {}
+    for j, n in enumerate(names):
+        w = work[n]
+        t = mean_ms[j] * 1e-3
+        b, _ = roofline.bound(w["ops"], w["bytes"])
+        gbs = w["bytes"] / t / 1e9
+        tops = w["ops"] / t / 1e12
+        kernels[n] = {
+            "shape": w["shape"], "us": round(mean_ms[j] * 1e3, 2),
+            "us_min": round(dur_ms[:, j].min() * 1e3, 2),
+            "GB_per_s": round(gbs, 1), "TOPS": round(tops, 2), "bound": b,
+            "frac_of_bound": round(gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S if b == "hbm"
+                                   else tops * 1e12 / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4),
+        }
+
+    head = kernels["gemm_w4a8_m4096"]
+    gemv = kernels["gemm_w4a8_m1"]
+    roof = {
+        "bound": "mfma", "kernel": "gemm_w4a8_m4096 (gemm_tiled_kernel<4,256,256>)",
+        "achieved": head["TOPS"], "peak": roofline.INT8_MFMA_PEAK_OPS_PER_S / 1e12,
+        "unit": "TOPS", "frac": round(head["TOPS"] * 1e12 / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4),
+        "traffic": None,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A4096, B4v, s4, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": head["TOPS"],
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_ms_per_step, 4),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "launch_queue_prefilled": held,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "w4a8 dequant GEMM M=4096 N=4096 K=4096 within one pass of the path "
+                        "(quantize 12288x4096, w8a8 M=64, pack int4/int2, w4a8 M=1 and 4096, "
+                        "w2a8 M=1 and 128)",
+            "M": 4096, "N": 4096, "K": 4096, "weight_bits": 4,
+        },
+        "gemv_m1": {"GB_per_s": gemv["GB_per_s"], "frac_of_hbm_peak": gemv["frac_of_bound"],
+                    "us": gemv["us"], "shape": gemv["shape"],
+                    "sustained_us": round(gemv_sustained_us, 3),
+                    "sustained_GB_per_s": round(work["gemm_w4a8_m1"]["bytes"] / (gemv_sustained_us * 1e-6) / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(A, Bv, s, budget_s):
+    """The oracle (unpack -> integer GEMM -> dequant, as it stands) on a
+    bounded sample of rows of the M = 4096 W4A8 workload, on the host cores."""
+    import oracle
+
+    Bp = oracle.pack_int4(Bv)
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
+
+    def run(rows):
+        t = time.perf_counter()
+        oracle.gemm_wxa8_dequant(np.ascontiguousarray(A[:rows]), Bp, s, 4)
+        return time.perf_counter() - t
+
+    rows = 8
+    t = run(rows)
+    rows = int(min(A.shape[0], max(8, rows * budget_s / max(t, 1e-3))))
+    t = run(rows)
+    ops = 2 * rows * Bv.shape[0] * Bv.shape[1]
+    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} of 4096 rows of A (M={rows}, N=4096, K=4096, w4a8 dequant), "
+                      f"{t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

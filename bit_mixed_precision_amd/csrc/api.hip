@@ -1,0 +1,211 @@
+// C ABI of libbq.so (declared in include/bq.h): host-side validation, the
+// one-time device check, M-dispatch between the two GEMM kernels, launch.
+//
+// Validation follows the contracts of the pages' own entry points: BMINF's
+// quantize() asserts dtypes and that the scale has the reduced shape, and
+// its igemm asserts contiguity, device and matching K ("BMINF的後訓練量化實現",
+// 實現代碼分析2); here each check returns a status instead of raising, and
+// all checks run before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/bq.h"
+#include "bq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return BQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return BQ_ERR_DEVICE;
+    int st = g_device_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return BQ_ERR_HIP;
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? BQ_OK : BQ_ERR_DEVICE;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? BQ_OK : BQ_ERR_HIP; }
+
+// Largest M handled by the streaming kernel.  Below the MI355X ridge point
+// (about 625 int8 ops per byte) the GEMM is bound by streaming B; at N = K =
+// 4096 the intensity reaches the ridge near M = 300, but the tiled kernel
+// already overlaps loads with matrix-core work from M of a few hundred down
+// to 128, and the streaming kernel's A re-reads grow with M.
+constexpr int64_t kStreamMaxM = 64;
+
+int validate_gemm(const int8_t *A, const void *B, int bits, const void *scale, void *C,
+                  int64_t M, int64_t N, int64_t K, int path)
+{
+    if (bits != 8 && bits != 4 && bits != 2)
+        return BQ_ERR_ARG;
+    if (path != BQ_PATH_AUTO && path != BQ_PATH_STREAM && path != BQ_PATH_TILED)
+        return BQ_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0 || K > BQ_MAX_K || (K % 64) != 0)
+        return BQ_ERR_SHAPE;
+    if (M > INT32_MAX || N > INT32_MAX)
+        return BQ_ERR_SHAPE;
+    if (path == BQ_PATH_STREAM && M > kStreamMaxM)
+        return BQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return BQ_OK;
+    if (!C || (K > 0 && (!A || !B)))
+        return BQ_ERR_NULL;
+    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))))
+        return BQ_ERR_ALIGN;
+    if (scale && !aligned16(scale))
+        return BQ_ERR_ALIGN;
+    return BQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bq_version(void) { return 100; }
+
+const char *bq_status_string(int status)
+{
+    switch (status) {
+    case BQ_OK: return "ok";
+    case BQ_ERR_NULL: return "a required pointer is NULL";
+    case BQ_ERR_SHAPE: return "invalid shape (negative dimension, divisibility or size limit)";
+    case BQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case BQ_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case BQ_ERR_DEVICE: return "the current device is not gfx950";
+    case BQ_ERR_ARG: return "invalid enumerated argument";
+    default: return "unknown status";
+    }
+}
+
+int bq_quantize_rows(const void *x_f16, int64_t rows, int64_t cols, int8_t *q,
+                     void *scale_f16, void *stream)
+{
+    if (rows < 0 || cols < 0 || rows > INT32_MAX)
+        return BQ_ERR_SHAPE;
+    if (rows == 0)
+        return BQ_OK;
+    if (!scale_f16 || (cols > 0 && (!x_f16 || !q)))
+        return BQ_ERR_NULL;
+    if (!aligned16(scale_f16) || (cols > 0 && (!aligned16(x_f16) || !aligned16(q))))
+        return BQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != BQ_OK)
+        return dev;
+    return launch_status(bq::launch_quantize_rows((const uint16_t *)x_f16, rows, cols, q,
+                                                  (uint16_t *)scale_f16, (hipStream_t)stream));
+}
+
+static int pack_common(const int8_t *v, int64_t n, int64_t k, uint8_t *out, int factor)
+{
+    if (n < 0 || k < 0 || (k % factor) != 0)
+        return BQ_ERR_SHAPE;
+    if (n == 0 || k == 0)
+        return BQ_OK;
+    if (!v || !out)
+        return BQ_ERR_NULL;
+    if (!aligned16(v) || !aligned16(out))
+        return BQ_ERR_ALIGN;
+    return check_device();
+}
+
+int bq_pack_int4(const int8_t *v, int64_t n, int64_t k, uint8_t *out, void *stream)
+{
+    const int st = pack_common(v, n, k, out, 2);
+    if (st != BQ_OK || n == 0 || k == 0)
+        return st;
+    return launch_status(bq::launch_pack_int4(v, n * k, out, (hipStream_t)stream));
+}
+
+int bq_pack_int2(const int8_t *v, int64_t n, int64_t k, uint8_t *out, void *stream)
+{
+    const int st = pack_common(v, n, k, out, 4);
+    if (st != BQ_OK || n == 0 || k == 0)
+        return st;
+    return launch_status(bq::launch_pack_int2(v, n * k, out, (hipStream_t)stream));
+}
+
+int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits)
+{
+    (void)N;
+    (void)K;
+    (void)bits;
+    return M <= kStreamMaxM ? BQ_PATH_STREAM : BQ_PATH_TILED;
+}
+
+int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,
+            int64_t M, int64_t N, int64_t K, int path, void *stream)
+{
+    int st = validate_gemm(A, B, bits, scale_f16, C, M, N, K, path);
+    if (st != BQ_OK || M == 0 || N == 0)
+        return st;
+    st = check_device();
+    if (st != BQ_OK)
+        return st;
+    if (path == BQ_PATH_AUTO)
+        path = bq_gemm_select_path(M, N, K, bits);
+    const hipStream_t s = (hipStream_t)stream;
+    const uint8_t *Bb = (const uint8_t *)B;
+    const uint16_t *sc = (const uint16_t *)scale_f16;
+    if (path == BQ_PATH_STREAM)
+        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, C, (int)M, (int)N, (int)K, s));
+    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, C, (int)M, (int)N, (int)K, s));
+}
+
+int bq_gemm_w8a8_dequant(const int8_t *A, const int8_t *B, const void *scale_f16,
+                         void *C_f16, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (!scale_f16 && M > 0 && N > 0)
+        return BQ_ERR_NULL;
+    return bq_gemm(A, B, 8, scale_f16, C_f16, M, N, K, BQ_PATH_AUTO, stream);
+}
+
+int bq_gemm_w4a8_dequant(const int8_t *A, const uint8_t *B, const void *scale_f16,
+                         void *C_f16, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (!scale_f16 && M > 0 && N > 0)
+        return BQ_ERR_NULL;
+    return bq_gemm(A, B, 4, scale_f16, C_f16, M, N, K, BQ_PATH_AUTO, stream);
+}
+
+int bq_gemm_w2a8_dequant(const int8_t *A, const uint8_t *B, const void *scale_f16,
+                         void *C_f16, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (!scale_f16 && M > 0 && N > 0)
+        return BQ_ERR_NULL;
+    return bq_gemm(A, B, 2, scale_f16, C_f16, M, N, K, BQ_PATH_AUTO, stream);
+}
+
+int bq_gemm_w8a8_i32(const int8_t *A, const int8_t *B, int32_t *C_i32,
+                     int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return bq_gemm(A, B, 8, nullptr, C_i32, M, N, K, BQ_PATH_AUTO, stream);
+}
+
+int bq_gemm_w4a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
+                     int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return bq_gemm(A, B, 4, nullptr, C_i32, M, N, K, BQ_PATH_AUTO, stream);
+}
+
+int bq_gemm_w2a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
+                     int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return bq_gemm(A, B, 2, nullptr, C_i32, M, N, K, BQ_PATH_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Internal declarations shared by the HIP translation units of libbq.so.
+// Not installed; the public interface is include/bq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint (data read once: streamed weights
+// and activations that should not displace reused lines in the caches).
+__device__ __forceinline__ uint4 load_nt16(const void *p)
+{
+    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Kernel launchers.  Arguments have been validated by the C ABI layer:
+// sizes are non-negative and within limits, pointers non-null and aligned.
+// Each returns the status of the launch (hipGetLastError after it).
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
+                                int8_t *q, uint16_t *scale, hipStream_t s);
+hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
+hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
+
+// Streaming skinny-M GEMM, M <= 64.  scale == nullptr selects int32 output.
+hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
+                              const uint16_t *scale, void *C,
+                              int M, int N, int K, hipStream_t s);
+// LDS-tiled matrix-core GEMM, any M.
+hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
+                             const uint16_t *scale, void *C,
+                             int M, int N, int K, hipStream_t s);
+
+}  // namespace bq

@@ -1,0 +1,186 @@
+// Per-row symmetric int8 quantization of an fp16 matrix.
+//
+// BMINF post-training quantization page ("BMINF的後訓練量化實現"), section
+// 實現代碼分析2: the quantize() docstring runs two kernels, a per-row
+// absmax reduction giving scale = absmax/127 in fp16, then an elementwise
+// copy giving the nearest integer of x/scale as int8.  Here both are one
+// kernel: a workgroup owns a row, keeps it in registers, reduces the absmax
+// (wavefront shuffles, then LDS across the four wavefronts) and writes the
+// codes, so x is read from HBM once.
+//
+// Rounding: the code is the nearest integer to the EXACT quotient x/scale,
+// ties to even, clamped to [-127, 127].  Without a division per element:
+//   q0 = rint(x * r), r = 1/scale rounded to fp32.
+// x and scale are fp16 values (11 significant bits), so a quotient that is
+// not exactly a half-integer lies at least 2^-13 from every half-integer,
+// while x*r is within 190 * 2^-23 of the quotient; q0 is then exact.  For
+// an exact half-integer (a tie) the residual e = x - q0*scale, computed
+// exactly by one fma (q0*scale has at most 19 significant bits), equals
+// +-scale/2, and q0 is moved to the even neighbour if it is odd.
+// The scale itself is fp16(absmax / 127): fp32 division rounded once more
+// to fp16 equals the correctly rounded quotient for every fp16 absmax (the
+// quotient has a repeating binary expansion of period 7 unless exact, so
+// it never sits within fp32 precision of an fp16 midpoint).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "bq_internal.h"
+
+namespace bq {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t absmax2(uint32_t acc, uint32_t w)
+{
+    // |x| of fp16 data orders like its magnitude bits as unsigned integers.
+    u16x2 a = __builtin_bit_cast(u16x2, acc);
+    u16x2 b = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h)
+{
+    return __half2float(__ushort_as_half((unsigned short)h));
+}
+
+__device__ __forceinline__ int code_of(float x, float s, float r, float hs)
+{
+    float q0 = __builtin_rintf(x * r);
+    float e = __builtin_fmaf(-q0, s, x);
+    int q = (int)q0;
+    if (__builtin_fabsf(e) == hs && (q & 1))
+        q += (e > 0.f) ? 1 : -1;
+    return min(max(q, -127), 127);
+}
+
+// Row absmax over the workgroup; every thread gets the result.
+__device__ __forceinline__ uint32_t block_absmax(uint32_t m, uint32_t *red)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        red[wave] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    return m;
+}
+
+struct RowScale {
+    float s, r, hs;
+    bool zero;
+};
+
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits, uint16_t *scale_out)
+{
+    const float a = half_bits_to_float(amax_bits);
+    const __half sh = __float2half_rn(__fdiv_rn(a, 127.0f));
+    if (threadIdx.x == 0)
+        *scale_out = __half_as_ushort(sh);
+    RowScale rs;
+    rs.s = __half2float(sh);
+    rs.zero = (rs.s == 0.0f);
+    rs.r = rs.zero ? 0.0f : __fdiv_rn(1.0f, rs.s);
+    rs.hs = 0.5f * rs.s;
+    return rs;
+}
+
+__device__ __forceinline__ uint32_t codes4(uint32_t w0, uint32_t w1, const RowScale &rs)
+{
+    const int c0 = code_of(half_bits_to_float(w0 & 0xFFFF), rs.s, rs.r, rs.hs);
+    const int c1 = code_of(half_bits_to_float(w0 >> 16), rs.s, rs.r, rs.hs);
+    const int c2 = code_of(half_bits_to_float(w1 & 0xFFFF), rs.s, rs.r, rs.hs);
+    const int c3 = code_of(half_bits_to_float(w1 >> 16), rs.s, rs.r, rs.hs);
+    return (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
+           ((uint32_t)(c2 & 0xFF) << 16) | ((uint32_t)(c3 & 0xFF) << 24);
+}
+
+// Vector path: cols % 8 == 0, so a row is whole 16-byte vectors of 8 fp16
+// and its codes whole 8-byte words.  Thread t owns vectors t, t+256, ...
+// (consecutive threads read consecutive 16 bytes).  VPT vectors per thread
+// cover rows of up to 2048*VPT elements, held in registers.
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void quantize_rows_vec(
+    const uint4 *__restrict__ x, int64_t cols, uint2 *__restrict__ q,
+    uint16_t *__restrict__ scale)
+{
+    __shared__ uint32_t red[4];
+    const int64_t row = blockIdx.x;
+    const int nvec = (int)(cols >> 3);
+    const uint4 *xr = x + row * nvec;
+    uint2 *qr = q + row * nvec;
+
+    uint4 v[VPT];
+    uint32_t m2 = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int idx = threadIdx.x + j * kThreads;
+        v[j] = (idx < nvec) ? load_nt16(xr + idx) : make_uint4(0, 0, 0, 0);
+        m2 = absmax2(m2, v[j].x);
+        m2 = absmax2(m2, v[j].y);
+        m2 = absmax2(m2, v[j].z);
+        m2 = absmax2(m2, v[j].w);
+    }
+    const uint32_t amax = block_absmax(max(m2 & 0xFFFF, m2 >> 16), red);
+    const RowScale rs = row_scale(amax, scale + row);
+
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int idx = threadIdx.x + j * kThreads;
+        if (idx < nvec) {
+            uint2 out = make_uint2(0, 0);
+            if (!rs.zero) {
+                out.x = codes4(v[j].x, v[j].y, rs);
+                out.y = codes4(v[j].z, v[j].w, rs);
+            }
+            qr[idx] = out;
+        }
+    }
+}
+
+// General path for any cols (and rows too long for registers): two passes
+// over the row, the second normally served from L2.
+__global__ __launch_bounds__(kThreads) void quantize_rows_any(
+    const uint16_t *__restrict__ x, int64_t cols, int8_t *__restrict__ q,
+    uint16_t *__restrict__ scale)
+{
+    __shared__ uint32_t red[4];
+    const int64_t row = blockIdx.x;
+    const uint16_t *xr = x + row * cols;
+    int8_t *qr = q + row * cols;
+    uint32_t m = 0;
+    for (int64_t k = threadIdx.x; k < cols; k += kThreads)
+        m = max(m, (uint32_t)(xr[k] & 0x7FFF));
+    const uint32_t amax = block_absmax(m, red);
+    const RowScale rs = row_scale(amax, scale + row);
+    for (int64_t k = threadIdx.x; k < cols; k += kThreads)
+        qr[k] = rs.zero ? 0 : (int8_t)code_of(half_bits_to_float(xr[k]), rs.s, rs.r, rs.hs);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
+                                int8_t *q, uint16_t *scale, hipStream_t s)
+{
+    if (rows == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)rows), block(kThreads);
+    const int64_t nvec = cols / 8;
+    const bool vec = (cols % 8 == 0) && cols > 0;
+    if (vec && nvec <= 1 * kThreads)
+        quantize_rows_vec<1><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+    else if (vec && nvec <= 2 * kThreads)
+        quantize_rows_vec<2><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+    else if (vec && nvec <= 4 * kThreads)
+        quantize_rows_vec<4><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+    else if (vec && nvec <= 8 * kThreads)
+        quantize_rows_vec<8><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+    else
+        quantize_rows_any<<<grid, block, 0, s>>>(x, cols, q, scale);
+    return hipGetLastError();
+}
+
+}  // namespace bq

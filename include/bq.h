@@ -1,0 +1,180 @@
+/*
+ * bq.h - C ABI of the MI355X (gfx950) quantized GEMM library libbq.so.
+ *
+ * The library implements one hot path of low-bit LLM inference:
+ *
+ *   1. per-row symmetric int8 quantization of an fp16 matrix
+ *      (scale = absmax/127 as fp16, codes = nearest integer of x/scale);
+ *   2. packing of int8-held int4 / int2 weight values into bytes along K;
+ *   3. the mixed-precision GEMM
+ *        acc[m,n] = sum_k A[m,k] * B[n,k]            (int32)
+ *        C[m,n]   = fp16(acc[m,n] * scale[n])        (optional epilogue)
+ *      with A int8 [M,K] and B int8, int4 or int2 [N,K].
+ *
+ * Sources (page title, section):
+ *  - "BMINF的後訓練量化實現" (BMINF post-training quantization), 實現代碼分析2:
+ *    the quantize(x, out, scale, axis) contract and its two kernels
+ *    (per-row absmax/127 reduction, nearest-integer copy to int8), the
+ *    int8 weight [out, in] with fp16 scale [out, 1] parameter layout, and
+ *    the caller-allocated outputs of PartialAttention.quantize;
+ *  - "BitBLAS自定义操作开发指南：使用DSL扩展新的混合精度算子" (BitBLAS custom
+ *    operator guide), sections 1-2 and cases 1-2: int8 x int4 / int2 matmul
+ *    with int32 accumulation over K of B stored [N, K], dequantization by a
+ *    per-N fp16 scale with arguments ordered (A, B, scale, C), sub-byte
+ *    weights stored compressed as uint8 [N, K/2], and a dynamic range of M.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a HIP DEVICE pointer owned by the caller; the
+ *    library never frees or retains caller pointers.  Outputs must not
+ *    alias inputs.
+ *  - Every buffer is dense, row-major (C-contiguous) and 16-byte aligned.
+ *  - fp16 data is passed as void* holding IEEE binary16 bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous: they validate, enqueue kernels on `stream` and return;
+ *    the caller synchronizes.  A call on a stream is ordered with the
+ *    caller's other work on that stream.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued; a nonzero status means nothing was enqueued, except
+ *    BQ_ERR_HIP, which reports a failed launch.  Nothing aborts or throws
+ *    across the ABI.  A dimension of 0 (other than K) is a valid no-op.
+ *  - The device must be gfx950 (BQ_ERR_DEVICE otherwise); the check is made
+ *    once per device.
+ *  - Thread safety: calls are reentrant; the only shared state is a cached
+ *    per-device property record, written once.
+ */
+#ifndef BQ_H
+#define BQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bq_status {
+    BQ_OK = 0,
+    BQ_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    BQ_ERR_SHAPE = 2,  /* negative dimension, or a divisibility / size limit  */
+    BQ_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                    */
+    BQ_ERR_HIP = 4,    /* a HIP runtime call or kernel launch failed          */
+    BQ_ERR_DEVICE = 5, /* the current device is not gfx950                    */
+    BQ_ERR_ARG = 6     /* an enumerated argument (bits, path) is invalid      */
+};
+
+/* Largest K accepted by the GEMMs.  With int8 operands the int32 sum is
+ * bounded by K * 128 * 128, which stays below 2^31 for K <= 131071; the
+ * limit leaves a factor of two of headroom. */
+#define BQ_MAX_K 65536
+
+/* GEMM path selection for bq_gemm (the named GEMM calls use BQ_PATH_AUTO). */
+enum bq_path {
+    BQ_PATH_AUTO = 0,   /* choose by M (see bq_gemm_select_path)              */
+    BQ_PATH_STREAM = 1, /* streaming skinny-M kernel, M <= 64                 */
+    BQ_PATH_TILED = 2   /* LDS-tiled matrix-core kernel, any M                */
+};
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int bq_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *bq_status_string(int status);
+
+/*
+ * bq_quantize_rows - per-row symmetric int8 quantization.
+ * BMINF page, 實現代碼分析2, quantize() docstring (kernels
+ * bms_quantize_scale and bms_quantize_copy_half), reading: the code is the
+ * nearest integer to the EXACT quotient x/scale with ties to even, clamped
+ * to [-127, 127]; a row whose scale rounds to 0 gets codes 0.
+ *
+ *   x_f16     [rows, cols] fp16 input (finite values; NaN/Inf give
+ *             unspecified codes for that row)
+ *   q         [rows, cols] int8 output codes
+ *   scale_f16 [rows]       fp16 output, fp16(absmax_row / 127) rounded to
+ *                          nearest even
+ * rows, cols >= 0.  cols == 0 writes scale 0 for every row.
+ * Any cols is accepted; 16-byte alignment is required of x and q.
+ */
+int bq_quantize_rows(const void *x_f16, int64_t rows, int64_t cols,
+                     int8_t *q, void *scale_f16, void *stream);
+
+/*
+ * bq_pack_int4 - pack int4 values held one per int8 into bytes along K.
+ * BitBLAS guide, case 2 (uint8 [N, K/2] compressed storage); bit order:
+ * byte [n, k/2] = (v[n,k] & 0xF) | (v[n,k+1] & 0xF) << 4 for even k.
+ *
+ *   v   [n, k]   int8 values, expected in [-8, 7]; for values outside that
+ *                range the low four bits are stored
+ *   out [n, k/2] uint8
+ * k must be even (BQ_ERR_SHAPE otherwise).
+ */
+int bq_pack_int4(const int8_t *v, int64_t n, int64_t k, uint8_t *out, void *stream);
+
+/*
+ * bq_pack_int2 - pack 2-bit (BitNet-b1.58 ternary) values along K.
+ * BitBLAS guide, case 1 (int2 weights); bit order: byte [n, k/4] holds the
+ * code v[n, k+j] + 2 in bits 2j..2j+1, j = 0..3 (lowest bits = lowest k).
+ *
+ *   v   [n, k]   int8 values, expected in [-2, 1] (ternary data: -1, 0, 1);
+ *                outside that range the low two bits of v+2 are stored
+ *   out [n, k/4] uint8
+ * k must be a multiple of 4.
+ */
+int bq_pack_int2(const int8_t *v, int64_t n, int64_t k, uint8_t *out, void *stream);
+
+/*
+ * bq_gemm_w{8,4,2}a8_dequant - C = fp16((A . B^T as int32) * scale[n]).
+ * BitBLAS guide, section 2 (create_dequantize_matmul), arguments in its
+ * order (A, B, scale, C).  The epilogue multiplies in fp32 and rounds to
+ * fp16 once (nearest even): the result is within one fp16 ulp of the
+ * correctly rounded product, and |acc*scale| >= 65520 gives +-inf.
+ *
+ *   A         [M, K]            int8, row-major
+ *   B         w8: int8 [N, K];  w4: uint8 [N, K/2] (bq_pack_int4 layout);
+ *             w2: uint8 [N, K/4] (bq_pack_int2 layout)
+ *   scale_f16 [N]               fp16
+ *   C_f16     [M, N]            fp16 output, row-major
+ * M, N >= 0; 0 <= K <= BQ_MAX_K and K % 64 == 0 (an implementation limit;
+ * pad K with zero columns of A otherwise).  K == 0 writes zeros.
+ */
+int bq_gemm_w8a8_dequant(const int8_t *A, const int8_t *B, const void *scale_f16,
+                         void *C_f16, int64_t M, int64_t N, int64_t K, void *stream);
+int bq_gemm_w4a8_dequant(const int8_t *A, const uint8_t *B, const void *scale_f16,
+                         void *C_f16, int64_t M, int64_t N, int64_t K, void *stream);
+int bq_gemm_w2a8_dequant(const int8_t *A, const uint8_t *B, const void *scale_f16,
+                         void *C_f16, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * bq_gemm_w{8,4,2}a8_i32 - C = A . B^T with the int32 accumulator as output.
+ * BitBLAS guide, section 1 and case 1 (create_mixed_precision_matmul,
+ * create_bitnet_int2_matmul).  Same operand layouts and limits as above;
+ * C_i32 [M, N] int32 row-major.  Exact (integer) for every valid input.
+ */
+int bq_gemm_w8a8_i32(const int8_t *A, const int8_t *B, int32_t *C_i32,
+                     int64_t M, int64_t N, int64_t K, void *stream);
+int bq_gemm_w4a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
+                     int64_t M, int64_t N, int64_t K, void *stream);
+int bq_gemm_w2a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
+                     int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * bq_gemm - the general form of the six GEMM calls above, with an explicit
+ * kernel path (BitBLAS guide, dynamic-shape section: kernels are chosen
+ * over a dynamic range of M).
+ *
+ *   bits       8, 4 or 2 (layout of B as above); BQ_ERR_ARG otherwise
+ *   scale_f16  [N] fp16, or NULL for the int32 output
+ *   C          fp16 [M, N] when scale_f16 != NULL, else int32 [M, N]
+ *   path       enum bq_path; BQ_PATH_STREAM requires M <= 64
+ */
+int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16,
+            void *C, int64_t M, int64_t N, int64_t K, int path, void *stream);
+
+/* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_STREAM or
+ * BQ_PATH_TILED).  Host-only integer logic; no device call. */
+int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQ_H */

@@ -1,0 +1,108 @@
+"""The C ABI library loads, exports every entry point declared in
+include/bq.h, and rejects invalid arguments on the host before any device
+call (no compute call is made here; these tests run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bq.h")
+
+
+@pytest.fixture(scope="module")
+def bq():
+    from bit_mixed_precision_amd import bq as _bq
+
+    if not os.path.exists(_bq.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return _bq
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(bq):
+    names = _declared()
+    assert len(names) == 13, names
+    lib = ctypes.CDLL(bq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bq.SIGNATURES)
+
+
+def test_version_and_status_strings(bq):
+    assert bq.version() == 100
+    for st in range(7):
+        assert bq.status_string(st)
+    assert bq.status_string(0) == "ok"
+    assert "unknown" in bq.status_string(99)
+
+
+def test_select_path(bq):
+    assert bq.select_path(1, 4096, 4096, 4) == "stream"
+    assert bq.select_path(64, 12288, 4096, 8) == "stream"
+    assert bq.select_path(65, 4096, 4096, 4) == "tiled"
+    assert bq.select_path(4096, 4096, 4096, 2) == "tiled"
+
+
+# Fake, never-dereferenced device addresses: validation fails before any
+# HIP call, so nothing touches them.
+P16 = ctypes.c_void_p(0x1000)
+P16b = ctypes.c_void_p(0x2000)
+P16c = ctypes.c_void_p(0x3000)
+P16d = ctypes.c_void_p(0x4000)
+PODD = ctypes.c_void_p(0x1001)
+NULL = ctypes.c_void_p(0)
+
+
+def test_gemm_validation(bq):
+    L = bq.lib()
+    S = NULL  # stream
+    # bad bits / path
+    assert L.bq_gemm(P16, P16b, 3, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ARG
+    assert L.bq_gemm(P16, P16b, 4, P16c, P16d, 4, 4, 64, 7, S) == bq.BQ_ERR_ARG
+    # shapes
+    for M, N, K in [(-1, 4, 64), (4, -1, 64), (4, 4, -64), (4, 4, 32), (4, 4, 100),
+                    (4, 4, 65536 + 64), (2**31, 4, 64)]:
+        assert L.bq_gemm(P16, P16b, 8, P16c, P16d, M, N, K, 0, S) == bq.BQ_ERR_SHAPE, (M, N, K)
+    # the streaming kernel only takes M <= 64
+    assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 65, 4, 64, 1, S) == bq.BQ_ERR_SHAPE
+    # nulls
+    assert L.bq_gemm(NULL, P16b, 8, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm(P16, NULL, 8, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm(P16, P16b, 8, P16c, NULL, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm_w4a8_dequant(P16, P16b, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_NULL
+    # alignment
+    assert L.bq_gemm(PODD, P16b, 8, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm(P16, PODD, 8, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm(P16, P16b, 8, PODD, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm(P16, P16b, 8, P16c, PODD, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    # empty outputs are valid no-ops (no device call needed)
+    assert L.bq_gemm(NULL, NULL, 8, NULL, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
+    assert L.bq_gemm(NULL, NULL, 4, NULL, NULL, 4, 0, 64, 0, S) == bq.BQ_OK
+    assert L.bq_gemm_w2a8_i32(NULL, NULL, NULL, 0, 0, 0, S) == bq.BQ_OK
+
+
+def test_quantize_and_pack_validation(bq):
+    L = bq.lib()
+    S = NULL
+    assert L.bq_quantize_rows(P16, -1, 8, P16b, P16c, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_quantize_rows(P16, 4, -8, P16b, P16c, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_quantize_rows(NULL, 4, 8, P16b, P16c, S) == bq.BQ_ERR_NULL
+    assert L.bq_quantize_rows(P16, 4, 8, P16b, NULL, S) == bq.BQ_ERR_NULL
+    assert L.bq_quantize_rows(PODD, 4, 8, P16b, P16c, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_quantize_rows(NULL, 0, 8, NULL, NULL, S) == bq.BQ_OK
+    assert L.bq_pack_int4(P16, 4, 3, P16b, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_pack_int2(P16, 4, 6, P16b, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_pack_int4(P16, -4, 8, P16b, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_pack_int4(NULL, 4, 8, P16b, S) == bq.BQ_ERR_NULL
+    assert L.bq_pack_int2(P16, 4, 8, PODD, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_pack_int4(NULL, 0, 8, NULL, S) == bq.BQ_OK
+    assert L.bq_pack_int2(NULL, 4, 0, NULL, S) == bq.BQ_OK

@@ -1,0 +1,221 @@
+"""GPU parity of the W8A8 / W4A8 / W2A8 GEMMs against the oracle, through the
+C ABI.  int32 accumulators bit-exact; fp16 outputs within 1 ulp of the
+correctly rounded acc*scale (the epilogue multiplies in fp32).
+
+Small shapes span several tiles of both kernels with ragged M and N tails;
+the workload shapes run in the launch configuration the benchmark uses
+(automatic path selection) and are compared on sampled rows/columns that
+the oracle computes one by one."""
+import numpy as np
+import pytest
+
+import oracle
+from bit_mixed_precision_amd import synth
+from gpu_util import assert_f16_within_1ulp, banner, f16_bits, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def _make(bits, M, N, K, seed):
+    """Host inputs: A int8, B values, packed B (by the oracle), fp16 scale."""
+    if bits == 8:
+        A, Bv, s = synth.w8a8_case(M, N, K, seed)
+        Bp = Bv
+    elif bits == 4:
+        A, Bv, s = synth.w4a8_case(M, N, K, seed)
+        Bp = oracle.pack_int4(Bv)
+    else:
+        A, Bv, s = synth.w2a8_case(M, N, K, seed, ternary=(seed % 2 == 0))
+        Bp = oracle.pack_int2(Bv)
+    return A, Bv, Bp, s
+
+
+def _run(dev, bits, A, Bp, s, path):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    Ad, Bd, sd = to_dev(A, dev), to_dev(Bp, dev), to_dev(s, dev)
+    acc = bq.gemm(Ad, Bd, bits, None, path=path)
+    C = bq.gemm(Ad, Bd, bits, sd, path=path)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), f16_bits(C)
+
+
+def _check(acc, C, A, Bv, s, rows=None, cols=None, what=""):
+    """Compare (optionally a sample of rows/cols of) the GPU results with the
+    oracle computed on the same rows/cols."""
+    rows = np.arange(A.shape[0]) if rows is None else rows
+    cols = np.arange(Bv.shape[0]) if cols is None else cols
+    acc_ref = oracle.gemm_i32(np.ascontiguousarray(A[rows]), np.ascontiguousarray(Bv[cols]))
+    got = acc[np.ix_(rows, cols)]
+    if not np.array_equal(got, acc_ref):
+        bad = np.argwhere(got != acc_ref)
+        i, j = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} int32 results differ; first at row "
+                             f"{rows[i]} col {cols[j]}: got {got[i, j]} want {acc_ref[i, j]}")
+    C_ref = oracle.dequant(acc_ref, s[cols])
+    n1 = assert_f16_within_1ulp(C[np.ix_(rows, cols)], C_ref, what)
+    return n1
+
+
+SMALL = [(1, 16, 64), (1, 33, 128), (3, 100, 192), (16, 256, 256), (17, 48, 320),
+         (33, 100, 320), (64, 520, 1024), (5, 4099, 128)]
+TILED_ONLY = [(65, 300, 384), (130, 257, 256), (257, 513, 640), (300, 130, 64)]
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("path", ["stream", "tiled"])
+@pytest.mark.parametrize("shape", SMALL)
+def test_small_shapes_both_paths(dev, bits, path, shape):
+    M, N, K = shape
+    banner(f"gemm bits={bits} path={path} M={M} N={N} K={K}")
+    A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
+    acc, C = _run(dev, bits, A, Bp, s, path)
+    _check(acc, C, A, Bv, s, what=f"w{bits} {path} {shape}")
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("shape", TILED_ONLY)
+def test_small_shapes_tiled(dev, bits, shape):
+    M, N, K = shape
+    banner(f"gemm bits={bits} path=auto(tiled) M={M} N={N} K={K}")
+    A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
+    acc, C = _run(dev, bits, A, Bp, s, "auto")
+    _check(acc, C, A, Bv, s, what=f"w{bits} auto {shape}")
+
+
+def test_w4a8_16x256x256_full(dev):
+    """The small W4A8 case: M=16, N=256, K=256, seed 0, compared in full."""
+    banner("gemm w4a8 16x256x256 seed 0")
+    A, Bv, s = synth.w4a8_case(16, 256, 256, seed=0)
+    Bp = oracle.pack_int4(Bv)
+    acc, C = _run(dev, 4, A, Bp, s, "auto")
+    _check(acc, C, A, Bv, s, what="w4a8 16x256x256")
+
+
+@pytest.mark.parametrize("N", [4096, 11008])
+def test_decode_gemv_w4a8_full(dev, N):
+    banner(f"gemm w4a8 decode M=1 N={N} K=4096")
+    A, Bv, s = synth.w4a8_case(1, N, 4096, seed=0)
+    acc, C = _run(dev, 4, A, oracle.pack_int4(Bv), s, "auto")
+    _check(acc, C, A, Bv, s, what=f"w4a8 1x{N}x4096")
+
+
+@pytest.mark.parametrize("M", [1, 128])
+def test_ternary_w2a8_workload(dev, M):
+    banner(f"gemm w2a8 ternary M={M} N=4096 K=4096")
+    A, Bv, s = synth.w2a8_case(M, 4096, 4096, seed=0)
+    acc, C = _run(dev, 2, A, oracle.pack_int2(Bv), s, "auto")
+    g = np.random.default_rng(1)
+    cols = np.sort(g.choice(4096, 512, replace=False))
+    _check(acc, C, A, Bv, s, cols=cols, what=f"w2a8 {M}x4096x4096")
+
+
+def test_bminf_quantize_then_w8a8(dev):
+    """Quantized fused-QKV weight [12288, 4096] (codes and scales from the
+    oracle) times int8 activations, M=64."""
+    banner("gemm w8a8 bminf M=64 N=12288 K=4096")
+    W, A = synth.bminf_case()
+    q, s = oracle.quantize_rows(W)
+    acc, C = _run(dev, 8, A, q, s.view(np.float16), "auto")
+    g = np.random.default_rng(2)
+    cols = np.sort(np.concatenate([g.choice(12288, 1000, replace=False), [0, 12287]]))
+    _check(acc, C, A, q, s.view(np.float16), cols=np.unique(cols), what="w8a8 bminf")
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 256, 1024, 4096])
+def test_w4a8_prefill_sweep(dev, M):
+    banner(f"gemm w4a8 sweep M={M} N=4096 K=4096")
+    A, Bv, s = synth.w4a8_case(M, 4096, 4096, seed=0)
+    acc, C = _run(dev, 4, A, oracle.pack_int4(Bv), s, "auto")
+    g = np.random.default_rng(M)
+    rows = np.arange(M) if M <= 64 else np.unique(np.concatenate(
+        [g.choice(M, 48, replace=False), [0, M - 1]]))
+    cols = np.unique(np.concatenate([g.choice(4096, 1024, replace=False), [0, 4095]]))
+    _check(acc, C, A, Bv, s, rows=rows, cols=cols, what=f"w4a8 sweep M={M}")
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("path", ["stream", "tiled"])
+def test_k_zero_and_empty(dev, bits, path):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner(f"gemm K=0 / empty bits={bits} path={path}")
+    A = torch.zeros((3, 0), dtype=torch.int8, device=dev)
+    B = torch.zeros((5, 0), dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+    s = torch.ones((5,), dtype=torch.float16, device=dev)
+    C = bq.gemm(A, B, bits, s, out=torch.full((3, 5), 7.0, dtype=torch.float16, device=dev), path=path)
+    acc = bq.gemm(A, B, bits, None, out=torch.full((3, 5), 7, dtype=torch.int32, device=dev), path=path)
+    torch.cuda.synchronize()
+    assert not acc.cpu().numpy().any()
+    assert not f16_bits(C).any()
+    # M = 0 and N = 0 are no-ops
+    bq.gemm(torch.zeros((0, 64), dtype=torch.int8, device=dev),
+            torch.zeros((5, 64 * bits // 8), dtype=B.dtype, device=dev), bits, s, path=path)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("path", ["stream", "tiled"])
+def test_max_k_extremes(dev, bits, path):
+    """K = 65536 (the largest accepted) with the largest-magnitude operands."""
+    banner(f"gemm K=65536 extremes bits={bits} path={path}")
+    K = 65536
+    M, N = 3, 40
+    A = np.full((M, K), -128, np.int8)
+    A[1] = 127
+    A[2, ::2] = -128
+    A[2, 1::2] = 127
+    vmin = {8: -128, 4: -8, 2: -2}[bits]
+    vmax = {8: 127, 4: 7, 2: 1}[bits]
+    Bv = np.full((N, K), vmin, np.int8)
+    Bv[1::2] = vmax
+    Bv[5, :K // 2] = 0
+    Bp = Bv if bits == 8 else (oracle.pack_int4(Bv) if bits == 4 else oracle.pack_int2(Bv))
+    s = np.full(N, 2.0 ** -24, np.float16)
+    s[::3] = 2.0 ** -14
+    acc, C = _run(dev, bits, A, Bp, s, path)
+    _check(acc, C, A, Bv, s, what=f"K max w{bits} {path}")
+
+
+def test_named_entry_points_agree(dev):
+    """The six named calls give the results of the general call."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner("named entry points")
+    for bits in (8, 4, 2):
+        for M in (7, 100):
+            A, Bv, Bp, s = _make(bits, M, 200, 256, seed=bits + M)
+            Ad, Bd, sd = to_dev(A, dev), to_dev(Bp, dev), to_dev(s, dev)
+            acc = getattr(bq, f"gemm_w{bits}a8_i32")(Ad, Bd)
+            C = getattr(bq, f"gemm_w{bits}a8_dequant")(Ad, Bd, sd)
+            torch.cuda.synchronize()
+            _check(acc.cpu().numpy(), f16_bits(C), A, Bv, s, what=f"named w{bits} M={M}")
+
+
+def test_error_paths(dev):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner("error paths")
+    A = torch.zeros((4, 96), dtype=torch.int8, device=dev)
+    B = torch.zeros((4, 96), dtype=torch.int8, device=dev)
+    with pytest.raises(bq.BQError) as e:
+        bq.gemm(A, B, 8)  # K % 64 != 0
+    assert e.value.status == bq.BQ_ERR_SHAPE
+    buf = torch.zeros((4 * 64 + 1,), dtype=torch.int8, device=dev)
+    Au = buf[1:].view(4, 64)  # misaligned by one byte
+    with pytest.raises(bq.BQError) as e:
+        bq.gemm(Au, torch.zeros((4, 64), dtype=torch.int8, device=dev), 8)
+    assert e.value.status == bq.BQ_ERR_ALIGN
+    with pytest.raises(bq.BQError) as e:
+        bq.gemm(torch.zeros((65, 64), dtype=torch.int8, device=dev),
+                torch.zeros((4, 64), dtype=torch.int8, device=dev), 8, path="stream")
+    assert e.value.status == bq.BQ_ERR_SHAPE

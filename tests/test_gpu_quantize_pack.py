@@ -1,0 +1,115 @@
+"""GPU parity of the quantize and pack kernels against the oracle, through the
+C ABI (the thin binding).  Bit-exact: int8 codes, fp16 scales, packed bytes."""
+import numpy as np
+import pytest
+
+import oracle
+from bit_mixed_precision_amd import synth
+from gpu_util import banner, f16_bits, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def _quantize_case(dev, x16: np.ndarray, what: str):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner(f"quantize_rows {what} shape={x16.shape}")
+    q, s = bq.quantize_rows(to_dev(x16, dev))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows(x16)
+    assert np.array_equal(f16_bits(s), s_ref), f"{what}: scales differ"
+    qg = q.cpu().numpy()
+    if not np.array_equal(qg, q_ref):
+        bad = np.argwhere(qg != q_ref)
+        r, k = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} codes differ, first at {(r, k)}: "
+                             f"x={x16[r, k]!r} got {qg[r, k]} want {q_ref[r, k]}")
+
+
+def test_quantize_bminf_full(dev):
+    """The fused-QKV weight shape [3*4096, 4096] ~ N(0, 0.02), as timed."""
+    _quantize_case(dev, synth.bminf_weight(), "bminf 12288x4096")
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 7), (5, 8), (2, 2048), (7, 2056), (9, 1000),
+                                   (4, 4096), (3, 8192), (2, 16384), (2, 16392), (1, 40000),
+                                   (300, 64)])
+def test_quantize_shapes(dev, shape):
+    g = np.random.default_rng(shape[0] * 7 + shape[1])
+    x = (g.standard_normal(shape) * np.exp(g.uniform(-6, 6, (shape[0], 1)))).astype(np.float16)
+    _quantize_case(dev, x, "random")
+
+
+def test_quantize_special_rows(dev):
+    q = 2.0 ** -24
+    s0 = 2.0 ** -7
+    halves = [0.5, 1.5, 2.5, 3.5, 125.5, 126.5, -0.5, -1.5, -2.5, -126.5, 0, -0.0]
+    rows = np.zeros((6, 16), np.float64)
+    rows[0, :] = 0.0                              # all zero -> scale 0
+    rows[1, :4] = [63 * q, -63 * q, q, 0]         # scale underflows to 0
+    rows[2, :4] = [64 * q, -64 * q, 32 * q, q]    # subnormal scale
+    rows[3, :4] = [189 * q, -189 * q, 100 * q, 0]  # subnormal scale, clamped codes
+    rows[4, 0] = 127 * s0                         # exact ties x = (n + 1/2) * s
+    rows[4, 1:1 + len(halves)] = np.array(halves) * s0
+    rows[5, :] = np.linspace(-65504, 65504, 16)   # extremes
+    _quantize_case(dev, rows.astype(np.float16), "special rows")
+
+
+def test_quantize_ties_dense(dev):
+    """Rows where every element is an exact tie of the code rounding."""
+    s0 = 2.0 ** -6
+    n = np.arange(-127, 127) + 0.5
+    row = np.concatenate([[127 * s0], n * s0, [0.0]])
+    x = np.tile(row, (8, 1)).astype(np.float16)
+    _quantize_case(dev, x, "dense ties")
+
+
+def test_quantize_zero_cols(dev):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner("quantize_rows cols=0")
+    x = torch.zeros((5, 0), dtype=torch.float16, device=dev)
+    q, s = bq.quantize_rows(x)
+    torch.cuda.synchronize()
+    assert q.shape == (5, 0)
+    assert np.array_equal(f16_bits(s), np.zeros(5, np.uint16))
+
+
+@pytest.mark.parametrize("bits,shape", [(4, (4096, 4096)), (2, (4096, 4096)), (4, (11008, 4096)),
+                                        (4, (3, 10)), (2, (5, 12)), (4, (1, 2)), (2, (1, 4)),
+                                        (4, (7, 1000)), (2, (9, 1004))])
+def test_pack(dev, bits, shape):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner(f"pack_int{bits} shape={shape}")
+    g = synth.rng(shape[0] + bits)
+    v = synth.int4_values(g, shape) if bits == 4 else synth.int2_values(g, shape)
+    vd = to_dev(v, dev)
+    out = bq.pack_int4(vd) if bits == 4 else bq.pack_int2(vd)
+    torch.cuda.synchronize()
+    ref = oracle.pack_int4(v) if bits == 4 else oracle.pack_int2(v)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_pack_out_of_range_keeps_low_bits(dev):
+    """Outside the code range the header specifies the low bits are stored."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner("pack out-of-range values")
+    v = np.arange(-128, 128, dtype=np.int16).astype(np.int8).reshape(16, 16)
+    p4 = bq.pack_int4(to_dev(v, dev)).cpu().numpy()
+    p2 = bq.pack_int2(to_dev(v, dev)).cpu().numpy()
+    torch.cuda.synchronize()
+    lo4 = ((v.astype(np.int16) & 0xF) ^ 8) - 8          # low 4 bits, as int4
+    assert np.array_equal(p4, oracle.pack_int4(lo4.astype(np.int8)))
+    lo2 = (((v.astype(np.int16) + 2) & 3) - 2)          # low 2 bits of v+2, as a code
+    assert np.array_equal(p2, oracle.pack_int2(lo2.astype(np.int8)))
