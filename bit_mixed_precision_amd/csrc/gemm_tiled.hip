@@ -6,21 +6,32 @@
 // page's pattern: a wide accumulator, one downcast after the last K block),
 // optionally to C = fp16(acc * scale[n]) (BitBLAS guide, section 2).
 //
-// Decomposition (Pallas page, blocked matmul: output blocks independent,
-// the K blocks accumulated in sequence): a workgroup of four wavefronts owns
-// a BM x BN output tile and walks K in 128-byte steps.  Per step:
-//  * A (int8) and B (int8, or packed int4/int2 unpacked in registers on the
-//    way in, see unpack.h) are loaded from global memory with 16-byte loads
-//    and written to LDS as [row][128] int8 with the 16-byte chunk index
-//    XOR-swizzled by the row, so that the matrix-core operand reads of 32
-//    consecutive rows at one k offset spread over all banks;
-//  * LDS is double buffered: the global loads for step s+1 are issued before
-//    the matrix-core work of step s and stored after it; one barrier per
-//    step;
-//  * each wavefront computes a (BM/2) x (BN/2) quadrant with
-//    v_mfma_i32_32x32x32_i8 (the A operand gives 32 rows of A, the B operand
-//    32 rows of B; each lane's 16 operand bytes are 16 consecutive k, the
-//    same k for both operands).
+// Decomposition (Pallas page, blocked matmul: output blocks independent, the
+// K blocks accumulated in sequence): a workgroup of four wavefronts owns a
+// BM x BN output tile and walks K in stages of 128.
+//
+//  * Global -> LDS without registers: 16-byte buffer loads with the LDS-DMA
+//    form (lane i of a load writes LDS bytes [M0 + 16 i, +16)).  Rows past
+//    M / N and k past K are outside the buffer range and arrive as zeros.
+//    B stays packed in LDS (int4: 64 bytes per row per stage, int2: 32).
+//  * A ring of STAGES LDS buffers; the loads of stage s+STAGES-1 are issued
+//    while stage s is computed, so HBM/L2 latency is covered by whole stages.
+//  * Every LDS row is XOR-swizzled at 16-byte granularity so that the 16
+//    lanes served together by a 16-byte operand read hit 16 distinct 16-byte
+//    bank groups (rows of 128 / 64 / 32 bytes use the row bits above the
+//    2 / 4 / 8 rows that share one 256-byte bank line).  The load lanes are
+//    permuted so that the DMA writes exactly this layout.
+//  * Each wavefront computes a (BM/2) x (BN/2) quadrant with
+//    v_mfma_i32_32x32x32_i8, B fragments as the instruction's first operand
+//    (so the accumulator holds C transposed: each lane owns 4 consecutive n
+//    of one row m), A fragments as the second.  Per 32-k sub-step a lane
+//    feeds 16 consecutive k of each operand; packed B is read 16 bytes at a
+//    time and unpacked in registers (unpack.h) into 1, 2 or 4 sub-steps.
+//    Fragments of sub-step j+1 are read while the matrix cores run j.
+//  * One barrier per stage, placed between the two halves of the last
+//    sub-step so the next stage's first fragment reads overlap matrix work.
+//  * Epilogue: fp16(acc * scale) rows are staged through LDS and written
+//    with 16-byte coalesced stores.
 // Workgroups are mapped so that the tiles one XCD runs (blockIdx modulo 8
 // picks the XCD) form a compact block of the output, sharing A and B rows in
 // that XCD's L2.
@@ -33,31 +44,85 @@
 namespace bq {
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 constexpr int kThreads = 256;
-constexpr int kBK = 128;  // unpacked k per step = bytes per LDS row
+constexpr int kBK = 128;  // unpacked k per stage
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset that is always out of range
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
 
-template <int BITS, int BM, int BN, bool F16OUT>
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+typedef int v4si __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 layout): base address, stride 0, byte range,
+// default format word.  Offsets at or past `bytes` read as zero.
+__device__ __forceinline__ v4si make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    return (v4si){(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), (int)bytes, 0x00020000};
+}
+
+// 16-byte buffer load written straight to LDS: lane i stores its 16 bytes at
+// LDS address lds_addr + 16 i.  Issued as inline assembly so the compiler's
+// wait-count pass does not order every later LDS read behind it; the kernel
+// waits for these loads explicitly (wait_vmcnt) before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void dma16(v4si rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT>
+struct TiledCfg {
+    static constexpr int kPB = kBK * BITS / 8;          // packed B bytes per row per stage
+    static constexpr int kCPR = kPB / 16;               // B 16-byte chunks per row
+    static constexpr int kRowsPerLineB = 256 / kPB;     // B rows sharing a 256-byte bank line
+    static constexpr int kSwzShiftB = ilog2(kRowsPerLineB);
+    static constexpr int kSA = BM * kBK;                // A bytes per stage
+    static constexpr int kSB = BN * kPB;                // B bytes per stage
+    static constexpr int kStage = kSA + kSB;
+    static constexpr int kDmaA = kSA / 1024 / 4;        // DMA instructions per wave per stage
+    static constexpr int kDmaB = kSB / 1024 / 4;
+    static constexpr int kDma = kDmaA + kDmaB;
+    static constexpr int kFM = BM / 64;                 // 32x32 fragments per wave along M
+    static constexpr int kFN = BN / 64;                 // and N
+    static constexpr int kSPR = 8 / BITS;               // sub-steps fed by one packed 16-byte read
+    static constexpr int kWM = BM / 2, kWN = BN / 2;    // wave tile
+    // epilogue staging: 64 rows (or fewer) of kWN fp16 per wave, rows padded by 16 bytes
+    static constexpr int kEpiRows = kWM < 64 ? kWM : 64;
+    static constexpr int kEpiPitch = kWN * 2 + 16;
+    static constexpr int kEpiBytes = F16OUT ? 4 * kEpiRows * kEpiPitch : 0;
+    static constexpr int kLds = (STAGES * kStage > kEpiBytes) ? STAGES * kStage : kEpiBytes;
+    static_assert(kSB % 4096 == 0 && kSA % 4096 == 0, "each wave issues whole 1 KB DMA blocks");
+};
+
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL>
 __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, void *__restrict__ C, int M, int N, int K,
     int tilesM, int tilesN)
 {
     using U = Unpack<BITS>;
-    constexpr int kPB = kBK * BITS / 8;          // packed B bytes per row per step
-    constexpr int kCPR = kPB / 16;               // packed 16-byte chunks per row
-    constexpr int kBRowsPerPass = kThreads / kCPR;
-    constexpr int kBPasses = BN / kBRowsPerPass;
-    constexpr int kAPasses = BM / 32;            // A: 8 chunks per row, 32 rows per pass
-    constexpr int kUnpackChunks = 8 / BITS;      // LDS chunks produced per packed chunk
-    constexpr int kFM = BM / 64;                 // 32x32 fragments per wave, M
-    constexpr int kFN = BN / 64;                 // and N
-    static_assert(kBPasses >= 1 && BN % kBRowsPerPass == 0, "tile/pass mismatch");
+    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT>;
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
 
-    __shared__ __attribute__((aligned(16))) int8_t lds[2][(BM + BN) * kBK];
+    __shared__ __attribute__((aligned(1024))) int8_t lds[T::kLds];
 
     // ---- tile coordinates (XCD-aware) ----
     const int total = tilesM * tilesN;
@@ -73,135 +138,345 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // the wavefront index is uniform: keep it (and every LDS address derived
+    // from it) in scalar registers
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int64_t rowBytesB = (int64_t)K * BITS / 8;
+    const uint32_t rowBytesB = (uint32_t)((int64_t)K * BITS / 8);
     const int steps = (K + kBK - 1) / kBK;
 
-    // ---- global -> register staging ----
-    const int aChunk = tid & 7, aRow = tid >> 3;
-    const int bChunk = tid % kCPR, bRow = tid / kCPR;
-    uint4 ra[kAPasses], rb[kBPasses];
+    // Buffer resources over this tile's rows: rows past M / N are past the end.
+    const v4si srcA = make_rsrc(A + (int64_t)m0 * K, (uint32_t)(min(M - m0, BM) * K));
+    const v4si srcB = make_rsrc(B + (int64_t)n0 * rowBytesB, (uint32_t)min(N - n0, BN) * rowBytesB);
+    const uint32_t ldsBase = (uint32_t)(uintptr_t)(lds_void_t *)lds;
 
-    auto gload = [&](int step) {
-        const int k0 = step * kBK;
+    // ---- DMA address setup: lane -> (row, logical chunk) of each 1 KB block ----
+    // A block b (rows 8b..8b+7): lane s -> row 8b + s/8, physical chunk s%8.
+    const int aRowInBlk = lane >> 3;
+    uint32_t aOff[T::kDmaA];
+    int aChunkL[T::kDmaA];
 #pragma unroll
-        for (int p = 0; p < kAPasses; ++p) {
-            const int m = m0 + p * 32 + aRow;
-            const int k = k0 + aChunk * 16;
-            ra[p] = (m < M && k < K) ? *(const uint4 *)(A + (int64_t)m * K + k) : make_uint4(0, 0, 0, 0);
-        }
+    for (int p = 0; p < T::kDmaA; ++p) {
+        const int row = (wave + 4 * p) * 8 + aRowInBlk;
+        aChunkL[p] = (lane & 7) ^ ((row >> 1) & 7);
+        aOff[p] = (uint32_t)row * (uint32_t)K + aChunkL[p] * 16;
+    }
+    // B block b (1024 / kPB rows): lane s -> row (1024/kPB) b + s / kCPR, chunk s % kCPR.
+    constexpr int kBRowsPerBlk = 1024 / T::kPB;
+    uint32_t bOff[T::kDmaB];
+    int bChunkL[T::kDmaB];
 #pragma unroll
-        for (int p = 0; p < kBPasses; ++p) {
-            const int n = n0 + p * kBRowsPerPass + bRow;
-            const int64_t off = (int64_t)step * kPB + bChunk * 16;
-            rb[p] = (n < N && off < rowBytesB) ? *(const uint4 *)(B + (int64_t)n * rowBytesB + off)
-                                               : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto sstore = [&](int buf) {
-        int8_t *la = lds[buf];
-        int8_t *lb = lds[buf] + BM * kBK;
-#pragma unroll
-        for (int p = 0; p < kAPasses; ++p) {
-            const int row = p * 32 + aRow;
-            *(uint4 *)(la + row * kBK + swz(row, aChunk) * 16) = ra[p];
-        }
-#pragma unroll
-        for (int p = 0; p < kBPasses; ++p) {
-            const int row = p * kBRowsPerPass + bRow;
-            uint32_t o[U::kOutDwords];
-            U::run(rb[p], o);
-#pragma unroll
-            for (int u = 0; u < kUnpackChunks; ++u) {
-                const int chunk = bChunk * kUnpackChunks + u;
-                *(uint4 *)(lb + row * kBK + swz(row, chunk) * 16) =
-                    make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
-            }
-        }
-    };
-
-    v16i acc[kFM][kFN];
-#pragma unroll
-    for (int i = 0; i < kFM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFN; ++j)
-            acc[i][j] = (v16i){};
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    const int fr = lane & 31;  // operand row within a 32-row fragment
-    const int fg = lane >> 5;  // k half (16 bytes) within a 32-k sub-step
-    for (int step = 0; step < steps; ++step) {
-        const int buf = step & 1;
-        if (step + 1 < steps)
-            gload(step + 1);
-        const int8_t *la = lds[buf];
-        const int8_t *lb = lds[buf] + BM * kBK;
-#pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
-            const int chunk = ks * 2 + fg;
-            v4i a[kFM], b[kFN];
-#pragma unroll
-            for (int i = 0; i < kFM; ++i) {
-                const int row = wm * (BM / 2) + i * 32 + fr;
-                a[i] = *(const v4i *)(la + row * kBK + swz(row, chunk) * 16);
-            }
-#pragma unroll
-            for (int j = 0; j < kFN; ++j) {
-                const int row = wn * (BN / 2) + j * 32 + fr;
-                b[j] = *(const v4i *)(lb + row * kBK + swz(row, chunk) * 16);
-            }
-#pragma unroll
-            for (int i = 0; i < kFM; ++i)
-#pragma unroll
-                for (int j = 0; j < kFN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (step + 1 < steps)
-            sstore(buf ^ 1);
-        __syncthreads();
+    for (int p = 0; p < T::kDmaB; ++p) {
+        const int row = (wave + 4 * p) * kBRowsPerBlk + lane / T::kCPR;
+        bChunkL[p] = (lane % T::kCPR) ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1));
+        bOff[p] = (uint32_t)row * rowBytesB + bChunkL[p] * 16;
     }
 
+    // Loads of one stage.  Without a K tail (K % 128 == 0) the per-lane
+    // offsets are loop invariant and the stage's k offset travels in the
+    // scalar soffset; stages past the end re-read the last stage (in range,
+    // never consumed).  With a K tail, chunks past K get an out-of-range
+    // offset and read as zeros.
+    auto issue_stage = [&](int step, int part, int nparts) {
+        const uint32_t base = ldsBase + (uint32_t)((step % STAGES) * T::kStage);
+        const int sstep = min(step, steps - 1);
+        const int ka = sstep * kBK;
+        const uint32_t kb = (uint32_t)sstep * T::kPB;
+#pragma unroll
+        for (int p = 0; p < T::kDmaA; ++p) {
+            if (p % nparts != part)
+                continue;
+            uint32_t voff = aOff[p], soff = (uint32_t)ka;
+            if (KTAIL) {
+                voff = (ka + aChunkL[p] * 16 < K) ? aOff[p] + (uint32_t)ka : kOOB;
+                soff = 0;
+            }
+            dma16(srcA, base + (wave + 4 * p) * 1024, voff, soff);
+        }
+#pragma unroll
+        for (int p = 0; p < T::kDmaB; ++p) {
+            if ((T::kDmaA + p) % nparts != part)
+                continue;
+            uint32_t voff = bOff[p], soff = kb;
+            if (KTAIL) {
+                voff = (kb + bChunkL[p] * 16 < rowBytesB) ? bOff[p] + kb : kOOB;
+                soff = 0;
+            }
+            dma16(srcB, base + T::kSA + (wave + 4 * p) * 1024, voff, soff);
+        }
+    };
+
+    // ---- LDS -> operand fragments ----
+    const int fr = lane & 31;  // row within a 32-row fragment
+    const int fg = lane >> 5;  // lane group: which 16 k of a 32-k sub-step
+    v4i fa[2][T::kFM];         // A operand fragments, double buffered by sub-step
+    uint4 fbp[2][T::kFN];      // packed B, double buffered by packed read
+    auto read_a = [&](int step, int ks, int slot) {
+        const int8_t *la = lds + (step % STAGES) * T::kStage;
+        const int q = ks / T::kSPR, tt = ks % T::kSPR;
+        const int chunk = (2 * q + fg) * T::kSPR + tt;
+#pragma unroll
+        for (int i = 0; i < T::kFM; ++i) {
+            const int row = wm * T::kWM + i * 32 + fr;
+            fa[slot][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+        }
+    };
+    auto read_b = [&](int step, int q, int slot) {
+        const int8_t *lb = lds + (step % STAGES) * T::kStage + T::kSA;
+        const int chunk = 2 * q + fg;
+#pragma unroll
+        for (int j = 0; j < T::kFN; ++j) {
+            const int row = wn * T::kWN + j * 32 + fr;
+            fbp[slot][j] = *(const uint4 *)(lb + row * T::kPB +
+                                            ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+        }
+    };
+
+    v16i acc[T::kFM][T::kFN];
+#pragma unroll
+    for (int i = 0; i < T::kFM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::kFN; ++j)
+            acc[i][j] = (v16i){};
+
+    // B operands of sub-step ks, unpacked from the packed 16-byte read that
+    // feeds it (operand tt of that read)
+    v4i bop[2][T::kFN];
+    auto unpack_b = [&](int ks, int oslot) {
+        const int pslot = (ks / T::kSPR) & 1, tt = ks % T::kSPR;
+#pragma unroll
+        for (int j = 0; j < T::kFN; ++j) {
+            const uint4 &pk = fbp[pslot][j];
+            if constexpr (BITS == 8)
+                bop[oslot][j] = U::template operand<0>(pk);
+            else if constexpr (BITS == 4)
+                bop[oslot][j] = tt == 0 ? U::template operand<0>(pk) : U::template operand<1>(pk);
+            else
+                bop[oslot][j] = tt == 0 ? U::template operand<0>(pk)
+                              : tt == 1 ? U::template operand<1>(pk)
+                              : tt == 2 ? U::template operand<2>(pk)
+                                        : U::template operand<3>(pk);
+        }
+    };
+    // matrix-core work of one sub-step on fragment rows [i0, i1), B-fragment
+    // major so the first instructions need only the first unpacked B operand
+    auto mfma_rows = [&](int oslot, int aslot, int i0, int i1) {
+#pragma unroll
+        for (int j = 0; j < T::kFN; ++j)
+#pragma unroll
+            for (int i = i0; i < i1; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bop[oslot][j], fa[aslot][i], acc[i][j], 0, 0, 0);
+    };
+    constexpr int kHalf = T::kFM / 2;
+    constexpr int kReads = T::kFM + T::kFN;
+
+    // ---- prologue: stages 0 .. STAGES-2 in flight, stage 0 landed ----
+    issue_stage(0, 0, 1);
+    if (STAGES == 3)
+        issue_stage(1, 0, 1);
+    if (STAGES == 3)
+        wait_vmcnt<T::kDma>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+    read_b(0, 0, 0);
+    read_a(0, 0, 0);
+    asm volatile("" ::: "memory");
+
+    // ---- main loop (branch-free body) ----
+    // Sub-step ks runs the matrix cores on (fa[ks&1], bop[ks&1]) while the
+    // fragments of ks+1 are read and unpacked into the other slots (the first
+    // sub-step's B operands are unpacked at its start, fragment by fragment).
+    for (int step = 0; step < steps; ++step) {
+
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int cur = ks & 1;
+            if (ks == 0)
+                unpack_b(0, 0);  // this stage's first B operands (read after the last barrier)
+            if (ks < 3) {
+                if ((ks + 1) % T::kSPR == 0)
+                    read_b(step, (ks + 1) / T::kSPR, ((ks + 1) / T::kSPR) & 1);
+                read_a(step, ks + 1, cur ^ 1);
+                // a third of the loads for stage step+STAGES-1 (zeros past K)
+                issue_stage(step + STAGES - 1, ks, 3);
+                mfma_rows(cur, cur, 0, T::kFM);
+                unpack_b(ks + 1, cur ^ 1);
+#pragma unroll
+                for (int i = 0; i < kReads; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                }
+#pragma unroll
+                for (int i = kReads; i < T::kFM * T::kFN; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                mfma_rows(cur, cur, 0, kHalf);
+                __builtin_amdgcn_sched_barrier(0);
+                // stage step+1 has landed (only the loads issued this step may
+                // still be in flight) and every wave is done with stage step
+                if (STAGES == 3)
+                    wait_vmcnt<T::kDma>();
+                else
+                    wait_vmcnt<0>();
+                __syncthreads();
+                read_b(step + 1, 0, 0);
+                read_a(step + 1, 0, 0);
+                mfma_rows(cur, cur, kHalf, T::kFM);
+#pragma unroll
+                for (int i = 0; i < kReads; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("" ::: "memory");
+            }
+        }
+    }
+
+    // The loads issued in the last steps (zeros past K) must land before LDS
+    // is reused or the wavefront ends.
+    wait_vmcnt<0>();
+
     // ---- epilogue ----
-    // 32x32 output layout: lane l holds column l & 31; register r holds row
-    // 8*(r/4) + 4*(l >> 5) + (r & 3).
+    // Accumulator layout (C transposed): lane l of acc[i][j] holds row
+    // m = wm*kWM + 32 i + (l & 31) and, in registers 4g..4g+3, the four
+    // consecutive columns n = wn*kWN + 32 j + 8 g + 4 (l >> 5) + (0..3).
+    const int mrow = wm * T::kWM + fr;
+    if constexpr (F16OUT) {
+        // The lane's 4 x kFN groups of 4 consecutive scales, loaded together
+        // (one round trip) before the conversions.
+        const bool vecN = (N % 8) == 0;
+        uint2 sc[T::kFN][4];
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) {
-        const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-        float s = 0.f;
-        if (F16OUT && n < N)
-            s = __half2float(__ushort_as_half(scale[n]));
+        for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
-        for (int i = 0; i < kFM; ++i) {
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * T::kWN + j * 32 + 8 * g + 4 * fg;
+                if (vecN && n + 4 <= N) {
+                    sc[j][g] = *(const uint2 *)(scale + n);
+                } else {
+                    uint32_t h[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = (n + e < N) ? scale[n + e] : 0u;
+                    sc[j][g] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                }
+            }
+        __syncthreads();  // every wave is done with the stage buffers
+        int8_t *stg = lds + wave * T::kEpiRows * T::kEpiPitch;
+        constexpr int kChunksPerRow = T::kWN / 8;        // 16-byte chunks per staged row
+        constexpr int kRowsPerIt = 64 / kChunksPerRow;
+        constexpr int kFragsPerPass = T::kEpiRows / 32;
+#pragma unroll
+        for (int i0 = 0; i0 < T::kFM; i0 += kFragsPerPass) {
+#pragma unroll
+            for (int j = 0; j < T::kFN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = j * 32 + 8 * g + 4 * fg;  // first of 4 columns, wave-local
+                    // scale / 2^kShift folds the exact int4/int2 rescaling into
+                    // the multiply (a power-of-two factor, exact in fp32)
+                    constexpr float kInv = 1.0f / (float)(1 << U::kShift);
+                    float s[4];
+                    s[0] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x & 0xFFFF))) * kInv;
+                    s[1] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x >> 16))) * kInv;
+                    s[2] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y & 0xFFFF))) * kInv;
+                    s[3] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y >> 16))) * kInv;
+#pragma unroll
+                    for (int ii = 0; ii < kFragsPerPass; ++ii) {
+                        const int i = i0 + ii;
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            h[e] = __half_as_ushort(__float2half_rn((float)acc[i][j][4 * g + e] * s[e]));
+                        const int r = ii * 32 + fr;
+                        *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int it = 0; it < T::kEpiRows / kRowsPerIt; ++it) {
+                const int r = it * kRowsPerIt + lane / kChunksPerRow;
+                const int c = lane % kChunksPerRow;
+                const uint4 v = *(const uint4 *)(stg + r * T::kEpiPitch + c * 16);
+                const int m = m0 + wm * T::kWM + i0 * 32 + r;
+                const int n = n0 + wn * T::kWN + c * 8;
                 if (m < M && n < N) {
-                    const int v = acc[i][j][r] >> U::kShift;
-                    if (F16OUT)
-                        ((__half *)C)[(int64_t)m * N + n] = __float2half_rn((float)v * s);
-                    else
-                        ((int *)C)[(int64_t)m * N + n] = v;
+                    __half *dst = (__half *)C + (int64_t)m * N + n;
+                    if (vecN && n + 8 <= N) {
+                        *(uint4 *)dst = v;
+                    } else {
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e < N)
+                                ((uint16_t *)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        }
+    } else {
+        const bool vecN = (N % 4) == 0;
+#pragma unroll
+        for (int i = 0; i < T::kFM; ++i) {
+            const int m = m0 + mrow + i * 32;
+            if (m >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < T::kFN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * T::kWN + j * 32 + 8 * g + 4 * fg;
+                    int v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = acc[i][j][4 * g + e] >> U::kShift;
+                    int *dst = (int *)C + (int64_t)m * N + n;
+                    if (vecN && n + 4 <= N) {
+                        *(int4 *)dst = make_int4(v[0], v[1], v[2], v[3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N)
+                                dst[e] = v[e];
+                    }
                 }
             }
         }
     }
 }
 
-template <int BITS, int BM, int BN>
+template <int BITS, int BM, int BN, int STAGES>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
                     int M, int N, int K, hipStream_t s)
 {
     const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tilesM * tilesN));
-    if (scale)
-        gemm_tiled_kernel<BITS, BM, BN, true><<<grid, kThreads, 0, s>>>(A, B, scale, C, M, N, K, tilesM, tilesN);
-    else
-        gemm_tiled_kernel<BITS, BM, BN, false><<<grid, kThreads, 0, s>>>(A, B, scale, C, M, N, K, tilesM, tilesN);
+    const bool tail = (K % kBK) != 0;
+#define BQ_TILED_LAUNCH(F16, TAIL)                                                              \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL><<<grid, kThreads, 0, s>>>(A, B, scale, C, \
+                                                                               M, N, K, tilesM, tilesN)
+    if (scale) {
+        if (tail)
+            BQ_TILED_LAUNCH(true, true);
+        else
+            BQ_TILED_LAUNCH(true, false);
+    } else {
+        if (tail)
+            BQ_TILED_LAUNCH(false, true);
+        else
+            BQ_TILED_LAUNCH(false, false);
+    }
+#undef BQ_TILED_LAUNCH
     return hipGetLastError();
 }
 
@@ -209,11 +484,13 @@ template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
                        int M, int N, int K, hipStream_t s)
 {
-    // 256x256 tiles once there are enough of them to fill the 256 CUs.
+    // 256x256 tiles once there are enough of them to fill the 256 CUs.  Three
+    // LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
+    constexpr int kStages256 = BITS == 8 ? 2 : 3;
     const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (tiles256 >= 256)
-        return launch_t<BITS, 256, 256>(A, B, scale, C, M, N, K, s);
-    return launch_t<BITS, 128, 128>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 256, 256, kStages256>(A, B, scale, C, M, N, K, s);
+    return launch_t<BITS, 128, 128, 3>(A, B, scale, C, M, N, K, s);
 }
 
 }  // namespace

@@ -18,6 +18,8 @@
 
 #include <stdint.h>
 
+#include "bq_internal.h"
+
 namespace bq {
 
 // One packed dword (8 int4 values, k = 0..7) -> two dwords holding 16*v for
@@ -59,6 +61,13 @@ template <>
 struct Unpack<8> {
     static constexpr int kShift = 0;
     static constexpr int kOutDwords = 4;
+    // operand t (16 bytes = 16 k) of a 16-byte packed chunk
+    template <int TT>
+    __device__ __forceinline__ static v4i operand(const uint4 &p)
+    {
+        static_assert(TT == 0, "one operand per chunk");
+        return (v4i){(int)p.x, (int)p.y, (int)p.z, (int)p.w};
+    }
     __device__ __forceinline__ static void run(const uint4 &p, uint32_t *o)
     {
         o[0] = p.x;
@@ -72,6 +81,15 @@ template <>
 struct Unpack<4> {
     static constexpr int kShift = 4;
     static constexpr int kOutDwords = 8;
+    template <int TT>
+    __device__ __forceinline__ static v4i operand(const uint4 &p)
+    {
+        static_assert(TT == 0 || TT == 1, "two operands per chunk");
+        uint32_t o0, o1, o2, o3;
+        unpack8_int4(TT == 0 ? p.x : p.z, o0, o1);
+        unpack8_int4(TT == 0 ? p.y : p.w, o2, o3);
+        return (v4i){(int)o0, (int)o1, (int)o2, (int)o3};
+    }
     __device__ __forceinline__ static void run(const uint4 &p, uint32_t *o)
     {
         unpack8_int4(p.x, o[0], o[1]);
@@ -85,6 +103,14 @@ template <>
 struct Unpack<2> {
     static constexpr int kShift = 6;
     static constexpr int kOutDwords = 16;
+    template <int TT>
+    __device__ __forceinline__ static v4i operand(const uint4 &p)
+    {
+        static_assert(TT >= 0 && TT < 4, "four operands per chunk");
+        uint32_t o0, o1, o2, o3;
+        unpack16_int2(TT == 0 ? p.x : TT == 1 ? p.y : TT == 2 ? p.z : p.w, o0, o1, o2, o3);
+        return (v4i){(int)o0, (int)o1, (int)o2, (int)o3};
+    }
     __device__ __forceinline__ static void run(const uint4 &p, uint32_t *o)
     {
         unpack16_int2(p.x, o[0], o[1], o[2], o[3]);
