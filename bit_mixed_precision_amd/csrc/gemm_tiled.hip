@@ -46,7 +46,6 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;
 constexpr int kBK = 128;  // unpacked k per stage
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
@@ -88,8 +87,10 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT>
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES>
 struct TiledCfg {
+    static constexpr int kThreads = 64 * WAVES;
+    static constexpr int kWGN = WAVES / 2;              // wave grid: 2 along M, WAVES/2 along N
     static constexpr int kPB = kBK * BITS / 8;          // packed B bytes per row per stage
     static constexpr int kCPR = kPB / 16;               // B 16-byte chunks per row
     static constexpr int kRowsPerLineB = 256 / kPB;     // B rows sharing a 256-byte bank line
@@ -97,29 +98,31 @@ struct TiledCfg {
     static constexpr int kSA = BM * kBK;                // A bytes per stage
     static constexpr int kSB = BN * kPB;                // B bytes per stage
     static constexpr int kStage = kSA + kSB;
-    static constexpr int kDmaA = kSA / 1024 / 4;        // DMA instructions per wave per stage
-    static constexpr int kDmaB = kSB / 1024 / 4;
+    static constexpr int kDmaA = kSA / 1024 / WAVES;    // DMA instructions per wave per stage
+    static constexpr int kDmaB = kSB / 1024 / WAVES;
     static constexpr int kDma = kDmaA + kDmaB;
-    static constexpr int kFM = BM / 64;                 // 32x32 fragments per wave along M
-    static constexpr int kFN = BN / 64;                 // and N
+    static constexpr int kWM = BM / 2, kWN = BN / kWGN; // wave tile
+    static constexpr int kFM = kWM / 32;                // 32x32 fragments per wave along M
+    static constexpr int kFN = kWN / 32;                // and N
     static constexpr int kSPR = 8 / BITS;               // sub-steps fed by one packed 16-byte read
-    static constexpr int kWM = BM / 2, kWN = BN / 2;    // wave tile
     // epilogue staging: 64 rows (or fewer) of kWN fp16 per wave, rows padded by 16 bytes
     static constexpr int kEpiRows = kWM < 64 ? kWM : 64;
     static constexpr int kEpiPitch = kWN * 2 + 16;
-    static constexpr int kEpiBytes = F16OUT ? 4 * kEpiRows * kEpiPitch : 0;
+    static constexpr int kEpiBytes = F16OUT ? WAVES * kEpiRows * kEpiPitch : 0;
     static constexpr int kLds = (STAGES * kStage > kEpiBytes) ? STAGES * kStage : kEpiBytes;
-    static_assert(kSB % 4096 == 0 && kSA % 4096 == 0, "each wave issues whole 1 KB DMA blocks");
+    static_assert(kSB % (1024 * WAVES) == 0 && kSA % (1024 * WAVES) == 0, "each wave issues whole 1 KB DMA blocks");
+    static_assert(kFN >= 1 && kFM % 2 == 0, "wave tile");
 };
 
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL>
-__global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, void *__restrict__ C, int M, int N, int K,
     int tilesM, int tilesN)
 {
     using U = Unpack<BITS>;
-    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT>;
+    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES>;
+    constexpr int kThreads = T::kThreads;
     static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
 
     __shared__ __attribute__((aligned(1024))) int8_t lds[T::kLds];
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     // the wavefront index is uniform: keep it (and every LDS address derived
     // from it) in scalar registers
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::kWGN, wn = wave % T::kWGN;
 
     const uint32_t rowBytesB = (uint32_t)((int64_t)K * BITS / 8);
     const int steps = (K + kBK - 1) / kBK;
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     int aChunkL[T::kDmaA];
 #pragma unroll
     for (int p = 0; p < T::kDmaA; ++p) {
-        const int row = (wave + 4 * p) * 8 + aRowInBlk;
+        const int row = (wave + WAVES * p) * 8 + aRowInBlk;
         aChunkL[p] = (lane & 7) ^ ((row >> 1) & 7);
         aOff[p] = (uint32_t)row * (uint32_t)K + aChunkL[p] * 16;
     }
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     int bChunkL[T::kDmaB];
 #pragma unroll
     for (int p = 0; p < T::kDmaB; ++p) {
-        const int row = (wave + 4 * p) * kBRowsPerBlk + lane / T::kCPR;
+        const int row = (wave + WAVES * p) * kBRowsPerBlk + lane / T::kCPR;
         bChunkL[p] = (lane % T::kCPR) ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1));
         bOff[p] = (uint32_t)row * rowBytesB + bChunkL[p] * 16;
     }
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
                 voff = (ka + aChunkL[p] * 16 < K) ? aOff[p] + (uint32_t)ka : kOOB;
                 soff = 0;
             }
-            dma16(srcA, base + (wave + 4 * p) * 1024, voff, soff);
+            dma16(srcA, base + (wave + WAVES * p) * 1024, voff, soff);
         }
 #pragma unroll
         for (int p = 0; p < T::kDmaB; ++p) {
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
                 voff = (kb + bChunkL[p] * 16 < rowBytesB) ? bOff[p] + kb : kOOB;
                 soff = 0;
             }
-            dma16(srcB, base + T::kSA + (wave + 4 * p) * 1024, voff, soff);
+            dma16(srcB, base + T::kSA + (wave + WAVES * p) * 1024, voff, soff);
         }
     };
 
@@ -303,13 +306,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
                 issue_stage(step + STAGES - 1, ks, 3);
                 mfma_rows(cur, cur, 0, T::kFM);
                 unpack_b(ks + 1, cur ^ 1);
+                // all of the next sub-step's reads first (they have a whole
+                // sub-step to land), then the matrix work with the unpack
+                // of the next B operands interleaved
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
 #pragma unroll
-                for (int i = 0; i < kReads; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                }
-#pragma unroll
-                for (int i = kReads; i < T::kFM * T::kFN; ++i) {
+                for (int i = 0; i < T::kFM * T::kFN; ++i) {
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
                 }
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(
     }
 }
 
-template <int BITS, int BM, int BN, int STAGES>
+template <int BITS, int BM, int BN, int STAGES, int WAVES>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
                     int M, int N, int K, hipStream_t s)
 {
@@ -463,7 +465,7 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, vo
     const dim3 grid((unsigned)(tilesM * tilesN));
     const bool tail = (K % kBK) != 0;
 #define BQ_TILED_LAUNCH(F16, TAIL)                                                              \
-    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL><<<grid, kThreads, 0, s>>>(A, B, scale, C, \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES><<<grid, 64 * WAVES, 0, s>>>(A, B, scale, C, \
                                                                                M, N, K, tilesM, tilesN)
     if (scale) {
         if (tail)
@@ -489,8 +491,8 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     constexpr int kStages256 = BITS == 8 ? 2 : 3;
     const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (tiles256 >= 256)
-        return launch_t<BITS, 256, 256, kStages256>(A, B, scale, C, M, N, K, s);
-    return launch_t<BITS, 128, 128, 3>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, C, M, N, K, s);
+    return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, C, M, N, K, s);
 }
 
 }  // namespace
