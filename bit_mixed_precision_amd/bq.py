@@ -18,9 +18,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbq.so")
 
 BQ_OK, BQ_ERR_NULL, BQ_ERR_SHAPE, BQ_ERR_ALIGN, BQ_ERR_HIP, BQ_ERR_DEVICE, BQ_ERR_ARG = range(7)
-PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
+PATH_AUTO, PATH_STREAM, PATH_TILED, PATH_GEMV = 0, 1, 2, 3
 MAX_K = 65536
-_PATHS = {"auto": PATH_AUTO, "stream": PATH_STREAM, "tiled": PATH_TILED}
+_PATHS = {"auto": PATH_AUTO, "stream": PATH_STREAM, "tiled": PATH_TILED, "gemv": PATH_GEMV}
 
 # (name, argtypes) for every entry point declared in include/bq.h
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -77,7 +77,7 @@ def status_string(status: int) -> str:
 
 def select_path(M: int, N: int, K: int, bits: int) -> str:
     p = lib().bq_gemm_select_path(M, N, K, bits)
-    return {PATH_STREAM: "stream", PATH_TILED: "tiled"}[p]
+    return {PATH_STREAM: "stream", PATH_TILED: "tiled", PATH_GEMV: "gemv"}[p]
 
 
 # --------------------------------------------------------------------------
@@ -182,7 +182,7 @@ def _gemm_args(A, B, bits, scale, out):
 def gemm(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tensor] = None,
          out: Optional[torch.Tensor] = None, path: str = "auto") -> torch.Tensor:
     """C = A . B^T (int32), or fp16(C * scale[n]) when scale is given, with an
-    explicit kernel path ("auto", "stream" or "tiled").
+    explicit kernel path ("auto", "gemv", "stream" or "tiled").
 
     A int8 [M, K]; B int8 [N, K] (bits=8) or uint8 [N, K*bits/8] (bits=4, 2).
     """

@@ -69,8 +69,9 @@ enum bq_status {
 /* GEMM path selection for bq_gemm (the named GEMM calls use BQ_PATH_AUTO). */
 enum bq_path {
     BQ_PATH_AUTO = 0,   /* choose by M (see bq_gemm_select_path)              */
-    BQ_PATH_STREAM = 1, /* streaming skinny-M kernel, M <= 64                 */
-    BQ_PATH_TILED = 2   /* LDS-tiled matrix-core kernel, any M                */
+    BQ_PATH_STREAM = 1, /* streaming skinny-M matrix-core kernel, M <= 64     */
+    BQ_PATH_TILED = 2,  /* LDS-tiled matrix-core kernel, any M                */
+    BQ_PATH_GEMV = 3    /* decode GEMV on dot-product ALUs, M <= 4 (auto: M <= 2) */
 };
 
 /* Library version as an integer (major*10000 + minor*100 + patch). */
@@ -164,13 +165,14 @@ int bq_gemm_w2a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
  *   bits       8, 4 or 2 (layout of B as above); BQ_ERR_ARG otherwise
  *   scale_f16  [N] fp16, or NULL for the int32 output
  *   C          fp16 [M, N] when scale_f16 != NULL, else int32 [M, N]
- *   path       enum bq_path; BQ_PATH_STREAM requires M <= 64
+ *   path       enum bq_path; BQ_PATH_STREAM requires M <= 64, BQ_PATH_GEMV
+ *              requires M <= 4 (BQ_ERR_SHAPE otherwise)
  */
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16,
             void *C, int64_t M, int64_t N, int64_t K, int path, void *stream);
 
-/* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_STREAM or
- * BQ_PATH_TILED).  Host-only integer logic; no device call. */
+/* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_GEMV,
+ * BQ_PATH_STREAM or BQ_PATH_TILED).  Host-only integer logic; no device call. */
 int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits);
 
 #ifdef __cplusplus

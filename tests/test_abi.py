@@ -46,7 +46,9 @@ def test_version_and_status_strings(bq):
 
 
 def test_select_path(bq):
-    assert bq.select_path(1, 4096, 4096, 4) == "stream"
+    assert bq.select_path(1, 4096, 4096, 4) == "gemv"
+    assert bq.select_path(2, 4096, 4096, 2) == "gemv"
+    assert bq.select_path(3, 4096, 4096, 4) == "stream"
     assert bq.select_path(64, 12288, 4096, 8) == "stream"
     assert bq.select_path(65, 4096, 4096, 4) == "tiled"
     assert bq.select_path(4096, 4096, 4096, 2) == "tiled"
@@ -74,6 +76,8 @@ def test_gemm_validation(bq):
         assert L.bq_gemm(P16, P16b, 8, P16c, P16d, M, N, K, 0, S) == bq.BQ_ERR_SHAPE, (M, N, K)
     # the streaming kernel only takes M <= 64
     assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 65, 4, 64, 1, S) == bq.BQ_ERR_SHAPE
+    # the GEMV path only takes M <= 4
+    assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 5, 4, 64, 3, S) == bq.BQ_ERR_SHAPE
     # nulls
     assert L.bq_gemm(NULL, P16b, 8, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
     assert L.bq_gemm(P16, NULL, 8, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL

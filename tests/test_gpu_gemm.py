@@ -69,10 +69,12 @@ TILED_ONLY = [(65, 300, 384), (130, 257, 256), (257, 513, 640), (300, 130, 64)]
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
-@pytest.mark.parametrize("path", ["stream", "tiled"])
-@pytest.mark.parametrize("shape", SMALL)
-def test_small_shapes_both_paths(dev, bits, path, shape):
+@pytest.mark.parametrize("path", ["gemv", "stream", "tiled"])
+@pytest.mark.parametrize("shape", SMALL + [(2, 100, 64), (4, 37, 8192), (3, 4101, 640)])
+def test_small_shapes_all_paths(dev, bits, path, shape):
     M, N, K = shape
+    if path == "gemv" and M > 4:
+        pytest.skip("the GEMV path takes M <= 4")
     banner(f"gemm bits={bits} path={path} M={M} N={N} K={K}")
     A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
     acc, C = _run(dev, bits, A, Bp, s, path)
@@ -141,7 +143,7 @@ def test_w4a8_prefill_sweep(dev, M):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
-@pytest.mark.parametrize("path", ["stream", "tiled"])
+@pytest.mark.parametrize("path", ["gemv", "stream", "tiled"])
 def test_k_zero_and_empty(dev, bits, path):
     from bit_mixed_precision_amd import bq
     import torch
@@ -162,7 +164,7 @@ def test_k_zero_and_empty(dev, bits, path):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
-@pytest.mark.parametrize("path", ["stream", "tiled"])
+@pytest.mark.parametrize("path", ["gemv", "stream", "tiled"])
 def test_max_k_extremes(dev, bits, path):
     """K = 65536 (the largest accepted) with the largest-magnitude operands."""
     banner(f"gemm K=65536 extremes bits={bits} path={path}")
@@ -218,4 +220,8 @@ def test_error_paths(dev):
     with pytest.raises(bq.BQError) as e:
         bq.gemm(torch.zeros((65, 64), dtype=torch.int8, device=dev),
                 torch.zeros((4, 64), dtype=torch.int8, device=dev), 8, path="stream")
+    assert e.value.status == bq.BQ_ERR_SHAPE
+    with pytest.raises(bq.BQError) as e:
+        bq.gemm(torch.zeros((5, 64), dtype=torch.int8, device=dev),
+                torch.zeros((4, 64), dtype=torch.int8, device=dev), 8, path="gemv")
     assert e.value.status == bq.BQ_ERR_SHAPE
