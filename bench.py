@@ -44,7 +44,45 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed steps, run a plain 512 MiB device copy three times "
+                        "(the known-size reference for the HBM byte counters)")
     return p.parse_args()
+
+
+# Kernel sources of the tiled matrix-core GEMM; the committed HBM-traffic
+# summary is used only while these files are unchanged.
+TILED_SOURCES = ["gemm_tiled.hip", "unpack.h", "bq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a8_m4096_hbm_traffic.txt")
+
+
+def tiled_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in TILED_SOURCES:
+        with open(os.path.join(ROOT, "bit_mixed_precision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the M=4096 W4A8 GEMM from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by the copy-kernel factors), or
+    None if there is none or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    try:
+        if vals.get("source_sha256_16") != tiled_source_hash():
+            return None
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def ring_len(nbytes: int, minimum: int = 2) -> int:
@@ -187,6 +225,15 @@ def main():
     torch.cuda.synchronize()
     gemv_sustained_us = g0.elapsed_time(g1) * 1e3 / reps
 
+    kernel_path = {
+        "quantize_rows": "quantize", "pack_int4": "pack", "pack_int2": "pack",
+        "gemm_w8a8_m64": bq.select_path(64, 12288, K, 8),
+        "gemm_w4a8_m1": bq.select_path(1, 4096, K, 4),
+        "gemm_w4a8_m4096": bq.select_path(4096, 4096, K, 4),
+        "gemm_w2a8_m1": bq.select_path(1, 4096, K, 2),
+        "gemm_w2a8_m128": bq.select_path(128, 4096, K, 2),
+    }
+
     # ---------------- algorithmic work per kernel ----------------
     work = {
         "quantize_rows": dict(shape=[12288, 4096], bytes=roofline.quantize_bytes(12288, 4096), ops=0),
@@ -221,11 +268,23 @@ def main():
     head = kernels["gemm_w4a8_m4096"]
     gemv = kernels["gemm_w4a8_m1"]
     roof = {
-        "bound": "mfma", "kernel": "gemm_w4a8_m4096 (gemm_tiled_kernel<4,256,256>)",
+        "bound": "mfma", "kernel": "gemm_w4a8_m4096 (gemm_tiled_kernel, 256x256 tile, 8 waves)",
         "achieved": head["TOPS"], "peak": roofline.INT8_MFMA_PEAK_OPS_PER_S / 1e12,
         "unit": "TOPS", "frac": round(head["TOPS"] * 1e12 / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4),
-        "traffic": None,
+        "traffic": measured_traffic(),
+        "algorithmic_bytes": work["gemm_w4a8_m4096"]["bytes"],
     }
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for n in names:
+        kernels[n]["path"] = kernel_path[n]
 
     cpu = None
     if not args.no_cpu_baseline:
