@@ -41,12 +41,16 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? BQ_OK : BQ_ERR_HIP; }
 
-// Largest M handled by the streaming kernel.  Below the MI355X ridge point
-// (about 625 int8 ops per byte) the GEMM is bound by streaming B; at N = K =
-// 4096 the intensity reaches the ridge near M = 300, but the tiled kernel
-// already overlaps loads with matrix-core work from M of a few hundred down
-// to 128, and the streaming kernel's A re-reads grow with M.
+// Largest M handled by the streaming kernel (when asked for), and the largest
+// M for which automatic dispatch takes it.  Below the MI355X ridge point
+// (about 625 int8 ops per byte) the GEMM is bound by moving B; the streaming
+// kernel reads A from the caches once per matrix instruction, so its cost
+// grows with M, while the tiled kernel stages A through LDS.  Measured on
+// MI355X (W4A8, N = K = 4096): 5.8 / 9.0 / 13.5 us at M = 16 / 32 / 64 for
+// the streaming kernel against 11.2 / - / 12.1 us tiled; W8A8 at M = 64,
+// N = 12288: 28.6 us streaming, 15 us tiled.
 constexpr int64_t kStreamMaxM = 64;
+constexpr int64_t kStreamAutoMaxM = 32;
 // The dot-product GEMV accepts M <= 4 (each B byte feeds at most M
 // multiply-adds); automatic dispatch uses it up to M = 2, where it is faster
 // than the streaming matrix-core kernel (measured on MI355X at N = K = 4096:
@@ -155,7 +159,7 @@ int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits)
     (void)bits;
     if (M <= kGemvAutoMaxM)
         return BQ_PATH_GEMV;
-    return M <= kStreamMaxM ? BQ_PATH_STREAM : BQ_PATH_TILED;
+    return M <= kStreamAutoMaxM ? BQ_PATH_STREAM : BQ_PATH_TILED;
 }
 
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,

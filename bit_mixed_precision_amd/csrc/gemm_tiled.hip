@@ -7,13 +7,15 @@
 // optionally to C = fp16(acc * scale[n]) (BitBLAS guide, section 2).
 //
 // Decomposition (Pallas page, blocked matmul: output blocks independent, the
-// K blocks accumulated in sequence): a workgroup of four wavefronts owns a
-// BM x BN output tile and walks K in stages of 128.
+// K blocks accumulated in sequence): a workgroup owns a BM x BN output tile
+// (256 x 256 with eight wavefronts, 128 x 128 or 64 x 64 with four; chosen by
+// the number of tiles, see launch_bits) and walks K in stages of 128.
 //
 //  * Global -> LDS without registers: 16-byte buffer loads with the LDS-DMA
 //    form (lane i of a load writes LDS bytes [M0 + 16 i, +16)).  Rows past
 //    M / N and k past K are outside the buffer range and arrive as zeros.
 //    B stays packed in LDS (int4: 64 bytes per row per stage, int2: 32).
+//    The 1 KB blocks of a stage are dealt round-robin to the wavefronts.
 //  * A ring of STAGES LDS buffers; the loads of stage s+STAGES-1 are issued
 //    while stage s is computed, so HBM/L2 latency is covered by whole stages.
 //  * Every LDS row is XOR-swizzled at 16-byte granularity so that the 16
@@ -21,15 +23,17 @@
 //    bank groups (rows of 128 / 64 / 32 bytes use the row bits above the
 //    2 / 4 / 8 rows that share one 256-byte bank line).  The load lanes are
 //    permuted so that the DMA writes exactly this layout.
-//  * Each wavefront computes a (BM/2) x (BN/2) quadrant with
+//  * Wavefronts form a 2 x (WAVES/2) grid over the tile and compute with
 //    v_mfma_i32_32x32x32_i8, B fragments as the instruction's first operand
 //    (so the accumulator holds C transposed: each lane owns 4 consecutive n
 //    of one row m), A fragments as the second.  Per 32-k sub-step a lane
 //    feeds 16 consecutive k of each operand; packed B is read 16 bytes at a
 //    time and unpacked in registers (unpack.h) into 1, 2 or 4 sub-steps.
-//    Fragments of sub-step j+1 are read while the matrix cores run j.
-//  * One barrier per stage, placed between the two halves of the last
-//    sub-step so the next stage's first fragment reads overlap matrix work.
+//  * Wave tiles of several fragments read the fragments of sub-step j+1
+//    while the matrix cores run j, with one barrier per stage placed between
+//    the two halves of the last sub-step.  32 x 32 wave tiles (one matrix
+//    instruction per sub-step) instead read a whole stage of operands one
+//    stage ahead.
 //  * Epilogue: fp16(acc * scale) rows are staged through LDS and written
 //    with 16-byte coalesced stores.
 // Workgroups are mapped so that the tiles one XCD runs (blockIdx modulo 8
@@ -60,6 +64,7 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
 typedef int v4si __attribute__((ext_vector_type(4)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 // Raw buffer resource (gfx9 layout): base address, stride 0, byte range,
 // default format word.  Offsets at or past `bytes` read as zero.
@@ -87,6 +92,30 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// s_waitcnt with only the LDS / scalar-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt()
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
+// wait_vmcnt<F * c>() for a wave-uniform c in [0, C] (the counter limit must
+// be an immediate, so one branch per value).
+template <int F, int C>
+__device__ __forceinline__ void wait_vmcnt_rt(int c)
+{
+    if constexpr (C > 0) {
+        if (c == C) {
+            wait_vmcnt<F * C>();
+            return;
+        }
+        wait_vmcnt_rt<F, C - 1>(c);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
 template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES>
 struct TiledCfg {
     static constexpr int kThreads = 64 * WAVES;
@@ -98,9 +127,15 @@ struct TiledCfg {
     static constexpr int kSA = BM * kBK;                // A bytes per stage
     static constexpr int kSB = BN * kPB;                // B bytes per stage
     static constexpr int kStage = kSA + kSB;
-    static constexpr int kDmaA = kSA / 1024 / WAVES;    // DMA instructions per wave per stage
-    static constexpr int kDmaB = kSB / 1024 / WAVES;
-    static constexpr int kDma = kDmaA + kDmaB;
+    // 1 KB DMA blocks per stage, dealt round-robin to the wavefronts (block b
+    // to wave b % WAVES); when a count is not a multiple of WAVES the last
+    // round leaves some waves without a block
+    static constexpr int kBlkA = kSA / 1024;
+    static constexpr int kBlkB = kSB / 1024;
+    static constexpr int kDmaA = (kBlkA + WAVES - 1) / WAVES;  // block rounds per stage
+    static constexpr int kDmaB = (kBlkB + WAVES - 1) / WAVES;
+    static constexpr bool kEvenA = kBlkA % WAVES == 0, kEvenB = kBlkB % WAVES == 0;
+    static constexpr int kDma = kDmaA + kDmaB;          // DMA instructions per stage, upper bound per wave
     static constexpr int kWM = BM / 2, kWN = BN / kWGN; // wave tile
     static constexpr int kFM = kWM / 32;                // 32x32 fragments per wave along M
     static constexpr int kFN = kWN / 32;                // and N
@@ -110,8 +145,14 @@ struct TiledCfg {
     static constexpr int kEpiPitch = kWN * 2 + 16;
     static constexpr int kEpiBytes = F16OUT ? WAVES * kEpiRows * kEpiPitch : 0;
     static constexpr int kLds = (STAGES * kStage > kEpiBytes) ? STAGES * kStage : kEpiBytes;
-    static_assert(kSB % (1024 * WAVES) == 0 && kSA % (1024 * WAVES) == 0, "each wave issues whole 1 KB DMA blocks");
-    static_assert(kFN >= 1 && kFM % 2 == 0, "wave tile");
+    static_assert(kSA % 1024 == 0 && kSB % 1024 == 0, "whole 1 KB DMA blocks");
+    static_assert(kLds <= 160 * 1024, "LDS");
+    // 32 x 32 wave tiles read their operands a whole stage ahead instead of
+    // one sub-step ahead: a single matrix instruction per sub-step cannot
+    // cover the LDS latency.
+    static constexpr bool kAhead = kFM * kFN == 1;
+    static_assert(!kAhead || STAGES >= 4, "stage-ahead loop keeps STAGES-3 stages of loads in flight");
+    static_assert(kFN >= 1 && kFM >= 1 && (kFM == 1 || kFM % 2 == 0), "wave tile");
 };
 
 template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES>
@@ -123,7 +164,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     using U = Unpack<BITS>;
     using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES>;
     constexpr int kThreads = T::kThreads;
-    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+    static_assert(STAGES >= 2 && STAGES <= 8, "two to eight LDS stages");
+    static_assert((STAGES - 2) * T::kDma < 64, "outstanding loads fit the wait counter");
 
     __shared__ __attribute__((aligned(1024))) int8_t lds[T::kLds];
 
@@ -176,6 +218,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         bOff[p] = (uint32_t)row * rowBytesB + bChunkL[p] * 16;
     }
 
+    // This wavefront's DMA instructions per stage (wave-uniform).
+    int myDma = 0;
+#pragma unroll
+    for (int p = 0; p < T::kDmaA; ++p)
+        myDma += (wave + WAVES * p < T::kBlkA) ? 1 : 0;
+#pragma unroll
+    for (int p = 0; p < T::kDmaB; ++p)
+        myDma += (wave + WAVES * p < T::kBlkB) ? 1 : 0;
+    // Wait until the stage after the current one has landed: with an S-stage
+    // ring the loads of S-2 later stages (myDma each) may still be in flight.
+    auto wait_stage = [&]() {
+        if constexpr (T::kEvenA && T::kEvenB)
+            wait_vmcnt<(STAGES - 2) * T::kDma>();
+        else
+            wait_vmcnt_rt<STAGES - 2, T::kDma>(myDma);
+    };
+
     // Loads of one stage.  Without a K tail (K % 128 == 0) the per-lane
     // offsets are loop invariant and the stage's k offset travels in the
     // scalar soffset; stages past the end re-read the last stage (in range,
@@ -188,7 +247,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         const uint32_t kb = (uint32_t)sstep * T::kPB;
 #pragma unroll
         for (int p = 0; p < T::kDmaA; ++p) {
-            if (p % nparts != part)
+            if (p % nparts != part || (!T::kEvenA && wave + WAVES * p >= T::kBlkA))
                 continue;
             uint32_t voff = aOff[p], soff = (uint32_t)ka;
             if (KTAIL) {
@@ -199,7 +258,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         }
 #pragma unroll
         for (int p = 0; p < T::kDmaB; ++p) {
-            if ((T::kDmaA + p) % nparts != part)
+            if ((T::kDmaA + p) % nparts != part || (!T::kEvenB && wave + WAVES * p >= T::kBlkB))
                 continue;
             uint32_t voff = bOff[p], soff = kb;
             if (KTAIL) {
@@ -274,14 +333,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     constexpr int kHalf = T::kFM / 2;
     constexpr int kReads = T::kFM + T::kFN;
 
+    // The lane's 4 x kFN groups of 4 consecutive scales for the fp16
+    // epilogue, loaded before the K loop so their latency is hidden by it.
+    uint2 sc[F16OUT ? T::kFN : 1][4];
+    if constexpr (F16OUT) {
+        const bool vecS = (N % 8) == 0;
+#pragma unroll
+        for (int j = 0; j < T::kFN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * T::kWN + j * 32 + 8 * g + 4 * fg;
+                if (vecS && n + 4 <= N) {
+                    sc[j][g] = *(const uint2 *)(scale + n);
+                } else {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = (n + e < N) ? scale[n + e] : 0u;
+                    sc[j][g] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                }
+            }
+    }
+
+    if constexpr (!T::kAhead) {
     // ---- prologue: stages 0 .. STAGES-2 in flight, stage 0 landed ----
-    issue_stage(0, 0, 1);
-    if (STAGES == 3)
-        issue_stage(1, 0, 1);
-    if (STAGES == 3)
-        wait_vmcnt<T::kDma>();
-    else
-        wait_vmcnt<0>();
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        issue_stage(st, 0, 1);
+    wait_stage();
     __syncthreads();
     read_b(0, 0, 0);
     read_a(0, 0, 0);
@@ -321,10 +400,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 __builtin_amdgcn_sched_barrier(0);
                 // stage step+1 has landed (only the loads issued this step may
                 // still be in flight) and every wave is done with stage step
-                if (STAGES == 3)
-                    wait_vmcnt<T::kDma>();
-                else
-                    wait_vmcnt<0>();
+                wait_stage();
                 __syncthreads();
                 read_b(step + 1, 0, 0);
                 read_a(step + 1, 0, 0);
@@ -339,6 +415,88 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             }
         }
     }
+    } else {
+        // ---- stage-ahead loop (32 x 32 wave tiles): a wave's operands for a
+        // whole stage are read right after the barrier that publishes the
+        // stage, one stage before they are used.
+        constexpr int kPk = 4 / T::kSPR;  // packed B reads per stage
+        v4i ga[2][4][T::kFM];
+        uint4 gb[2][kPk][T::kFN];
+        auto read_stage = [&](int step, int slot) {
+            const int8_t *la = lds + (step % STAGES) * T::kStage;
+            const int8_t *lb = la + T::kSA;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int chunk = (2 * (ks / T::kSPR) + fg) * T::kSPR + ks % T::kSPR;
+#pragma unroll
+                for (int i = 0; i < T::kFM; ++i) {
+                    const int row = wm * T::kWM + i * 32 + fr;
+                    ga[slot][ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kPk; ++q) {
+                const int chunk = 2 * q + fg;
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j) {
+                    const int row = wn * T::kWN + j * 32 + fr;
+                    gb[slot][q][j] = *(const uint4 *)(lb + row * T::kPB +
+                                                      ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+                }
+            }
+        };
+        auto compute_stage = [&](int slot) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                v4i bo[T::kFN];
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j)
+                    bo[j] = U::operand_rt(gb[slot][ks / T::kSPR][j], ks % T::kSPR);
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j)
+#pragma unroll
+                    for (int i = 0; i < T::kFM; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bo[j], ga[slot][ks][i], acc[i][j], 0, 0, 0);
+            }
+        };
+        // One step: stage step+1 landed (the loads of STAGES-3 later stages
+        // may still be in flight) and this wave's reads of two steps ago done,
+        // then the barrier; after it, the loads of stage step+STAGES-1 go into
+        // the slot those reads used, the operands of stage step+1 are read
+        // and stage step is computed from the operands read one step ago.
+        // Only the reads of two steps ago are waited for at the barrier, so
+        // the latest reads stay in flight across it.  The scheduling fences
+        // keep the unpack of the operands just read (register work) from being
+        // hoisted next to the reads.  Unrolled by two so the operand slots are
+        // compile-time register indices.
+        constexpr int kReadsStep = 4 * T::kFM + kPk * T::kFN;
+        auto one_step = [&](int step, int cur) {
+            if constexpr (T::kEvenA && T::kEvenB)
+                wait_vmcnt<(STAGES - 3) * T::kDma>();
+            else
+                wait_vmcnt_rt<STAGES - 3, T::kDma>(myDma);
+            wait_lgkmcnt<kReadsStep>();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            issue_stage(step + STAGES - 1, 0, 1);
+            read_stage(step + 1, cur ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage(cur);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+#pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st)
+            issue_stage(st, 0, 1);
+        wait_stage();
+        __syncthreads();
+        read_stage(0, 0);
+        for (int step = 0; step < steps; step += 2) {
+            one_step(step, 0);
+            if (step + 1 < steps)
+                one_step(step + 1, 1);
+        }
+    }
 
     // The loads issued in the last steps (zeros past K) must land before LDS
     // is reused or the wavefront ends.
@@ -350,25 +508,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // consecutive columns n = wn*kWN + 32 j + 8 g + 4 (l >> 5) + (0..3).
     const int mrow = wm * T::kWM + fr;
     if constexpr (F16OUT) {
-        // The lane's 4 x kFN groups of 4 consecutive scales, loaded together
-        // (one round trip) before the conversions.
         const bool vecN = (N % 8) == 0;
-        uint2 sc[T::kFN][4];
-#pragma unroll
-        for (int j = 0; j < T::kFN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * T::kWN + j * 32 + 8 * g + 4 * fg;
-                if (vecN && n + 4 <= N) {
-                    sc[j][g] = *(const uint2 *)(scale + n);
-                } else {
-                    uint32_t h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        h[e] = (n + e < N) ? scale[n + e] : 0u;
-                    sc[j][g] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                }
-            }
         __syncthreads();  // every wave is done with the stage buffers
         int8_t *stg = lds + wave * T::kEpiRows * T::kEpiPitch;
         constexpr int kChunksPerRow = T::kWN / 8;        // 16-byte chunks per staged row
@@ -392,12 +532,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                     for (int ii = 0; ii < kFragsPerPass; ++ii) {
                         const int i = i0 + ii;
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            h[e] = __half_as_ushort(__float2half_rn((float)acc[i][j][4 * g + e] * s[e]));
+                        // pairs built as a two-element fp16 vector, so each
+                        // value is one fused multiply-convert into its half
+                        const h2v p01 = {(_Float16)((float)acc[i][j][4 * g + 0] * s[0]),
+                                         (_Float16)((float)acc[i][j][4 * g + 1] * s[1])};
+                        const h2v p23 = {(_Float16)((float)acc[i][j][4 * g + 2] * s[2]),
+                                         (_Float16)((float)acc[i][j][4 * g + 3] * s[3])};
                         const int r = ii * 32 + fr;
-                        *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                        *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) =
+                            make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
                     }
                 }
             }
@@ -482,17 +625,33 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, vo
     return hipGetLastError();
 }
 
+// Tile configuration by the number of output tiles; the 256 CUs want a few
+// hundred workgroups.  Measured on MI355X at N = K = 4096 (W4A8):
+//  * 256 x 256, eight wavefronts (2 x 4 of 128 x 64), once there are 256
+//    such tiles (M >= 4096);
+//  * 128 x 128, four wavefronts (64 x 64 each), from 192 tiles (M >= 768:
+//    25 us at M = 1024, 43 us at M = 2048 where the 256 x 256 tiles take 49);
+//  * 64 x 64, four wavefronts (32 x 32 each), a 4-stage ring, from 512 tiles
+//    (several workgroups per CU; 17 us at M = 512, against 22 us with
+//    128 x 128 tiles);
+//  * 64 x 64 with an 8-stage ring below that (12.3 us at M = 128, 12.9 us at
+//    M = 256, 15 us for W8A8 at M = 64, N = 12288; 21 us with 128 x 128).
 template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
                        int M, int N, int K, hipStream_t s)
 {
-    // 256x256 tiles once there are enough of them to fill the 256 CUs.  Three
-    // LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
+    // Three LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
     constexpr int kStages256 = BITS == 8 ? 2 : 3;
-    const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles256 >= 256)
+    const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+    if (t256 >= 256)
         return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, C, M, N, K, s);
-    return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, C, M, N, K, s);
+    if (t128 >= 192)
+        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, C, M, N, K, s);
+    if (t64 >= 512)
+        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, C, M, N, K, s);
+    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, C, M, N, K, s);
 }
 
 }  // namespace

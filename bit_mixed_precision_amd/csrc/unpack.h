@@ -68,6 +68,7 @@ struct Unpack<8> {
         static_assert(TT == 0, "one operand per chunk");
         return (v4i){(int)p.x, (int)p.y, (int)p.z, (int)p.w};
     }
+    __device__ __forceinline__ static v4i operand_rt(const uint4 &p, int) { return operand<0>(p); }
     __device__ __forceinline__ static void run(const uint4 &p, uint32_t *o)
     {
         o[0] = p.x;
@@ -90,6 +91,14 @@ struct Unpack<4> {
         unpack8_int4(TT == 0 ? p.y : p.w, o2, o3);
         return (v4i){(int)o0, (int)o1, (int)o2, (int)o3};
     }
+    // operand tt (0 or 1) chosen at run time: the two dwords are selected first
+    __device__ __forceinline__ static v4i operand_rt(const uint4 &p, int tt)
+    {
+        uint32_t o0, o1, o2, o3;
+        unpack8_int4(tt == 0 ? p.x : p.z, o0, o1);
+        unpack8_int4(tt == 0 ? p.y : p.w, o2, o3);
+        return (v4i){(int)o0, (int)o1, (int)o2, (int)o3};
+    }
     __device__ __forceinline__ static void run(const uint4 &p, uint32_t *o)
     {
         unpack8_int4(p.x, o[0], o[1]);
@@ -109,6 +118,13 @@ struct Unpack<2> {
         static_assert(TT >= 0 && TT < 4, "four operands per chunk");
         uint32_t o0, o1, o2, o3;
         unpack16_int2(TT == 0 ? p.x : TT == 1 ? p.y : TT == 2 ? p.z : p.w, o0, o1, o2, o3);
+        return (v4i){(int)o0, (int)o1, (int)o2, (int)o3};
+    }
+    // operand tt (0 .. 3) chosen at run time
+    __device__ __forceinline__ static v4i operand_rt(const uint4 &p, int tt)
+    {
+        uint32_t o0, o1, o2, o3;
+        unpack16_int2(tt == 0 ? p.x : tt == 1 ? p.y : tt == 2 ? p.z : p.w, o0, o1, o2, o3);
         return (v4i){(int)o0, (int)o1, (int)o2, (int)o3};
     }
     __device__ __forceinline__ static void run(const uint4 &p, uint32_t *o)

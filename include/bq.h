@@ -69,7 +69,7 @@ enum bq_status {
 /* GEMM path selection for bq_gemm (the named GEMM calls use BQ_PATH_AUTO). */
 enum bq_path {
     BQ_PATH_AUTO = 0,   /* choose by M (see bq_gemm_select_path)              */
-    BQ_PATH_STREAM = 1, /* streaming skinny-M matrix-core kernel, M <= 64     */
+    BQ_PATH_STREAM = 1, /* streaming skinny-M matrix-core kernel, M <= 64 (auto: M <= 32) */
     BQ_PATH_TILED = 2,  /* LDS-tiled matrix-core kernel, any M                */
     BQ_PATH_GEMV = 3    /* decode GEMV on dot-product ALUs, M <= 4 (auto: M <= 2) */
 };

@@ -49,8 +49,9 @@ def test_select_path(bq):
     assert bq.select_path(1, 4096, 4096, 4) == "gemv"
     assert bq.select_path(2, 4096, 4096, 2) == "gemv"
     assert bq.select_path(3, 4096, 4096, 4) == "stream"
-    assert bq.select_path(64, 12288, 4096, 8) == "stream"
-    assert bq.select_path(65, 4096, 4096, 4) == "tiled"
+    assert bq.select_path(32, 4096, 4096, 4) == "stream"
+    assert bq.select_path(33, 4096, 4096, 4) == "tiled"
+    assert bq.select_path(64, 12288, 4096, 8) == "tiled"
     assert bq.select_path(4096, 4096, 4096, 2) == "tiled"
 
 

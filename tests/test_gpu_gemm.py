@@ -91,6 +91,24 @@ def test_small_shapes_tiled(dev, bits, shape):
     _check(acc, C, A, Bv, s, what=f"w{bits} auto {shape}")
 
 
+# Shapes that select each tile configuration of the tiled path, with ragged
+# M, N and K tails: 256x256 tiles (4100x4100), 128x128 (1030x4100), 64x64
+# with a 4-stage ring (1000x2100, K tail of 64) and 64x64 with an 8-stage ring
+# (the rest; 100x200x1088 has a K tail, 3x40x8192 a long K).
+CFG_SHAPES = [(4100, 4100, 64), (1030, 4100, 128), (1000, 2100, 192), (200, 300, 1024),
+              (100, 200, 1088), (3, 40, 8192), (130, 257, 256)]
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("shape", CFG_SHAPES)
+def test_tile_configs_and_split_k(dev, bits, shape):
+    M, N, K = shape
+    banner(f"gemm bits={bits} path=tiled M={M} N={N} K={K}")
+    A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
+    acc, C = _run(dev, bits, A, Bp, s, "tiled")
+    _check(acc, C, A, Bv, s, what=f"w{bits} tiled {shape}")
+
+
 def test_w4a8_16x256x256_full(dev):
     """The small W4A8 case: M=16, N=256, K=256, seed 0, compared in full."""
     banner("gemm w4a8 16x256x256 seed 0")
