@@ -60,6 +60,7 @@ def _load():
             "bqref_unpack_int2": [P, I64, I64, P],
             "bqref_gemm_i32": [P, P, P, I64, I64, I64],
             "bqref_dequant": [P, P, P, I64, I64],
+            "bqref_dequant2": [P, P, P, P, I64, I64],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -204,6 +205,23 @@ def dequant(acc, scale) -> np.ndarray:
     return out
 
 
+def dequant2(acc, w_scale, x_scale) -> np.ndarray:
+    """fp16(acc[m,n] * w_scale[n] * x_scale[m]) correctly rounded; uint16 bits.
+
+    BMINF page, section 實現代碼分析2 (PartialAttention forward): per-token
+    activation scale times per-channel weight scale times the int32 result."""
+    acc = _c(acc, np.int32)
+    w_scale = _bits16(w_scale)
+    x_scale = _bits16(x_scale)
+    M, N = acc.shape
+    if w_scale.shape != (N,) or x_scale.shape != (M,):
+        raise ValueError("w_scale must be [N] and x_scale [M]")
+    out = np.empty((M, N), np.uint16)
+    _check(_load().bqref_dequant2(_ptr(acc), _ptr(w_scale), _ptr(x_scale), _ptr(out), M, N),
+           "dequant2")
+    return out
+
+
 def unpack(Bp, k: int, bits: int) -> np.ndarray:
     if bits == 8:
         return _c(Bp, np.int8)
@@ -224,3 +242,8 @@ def gemm_wxa8_i32(A, Bp, bits: int) -> np.ndarray:
 def gemm_wxa8_dequant(A, Bp, scale, bits: int) -> np.ndarray:
     """Steps unpack -> integer GEMM -> dequant; returns fp16 bits [M, N]."""
     return dequant(gemm_wxa8_i32(A, Bp, bits), scale)
+
+
+def gemm_wxa8_dequant2(A, Bp, w_scale, x_scale, bits: int) -> np.ndarray:
+    """Steps unpack -> integer GEMM -> two-scale dequant; fp16 bits [M, N]."""
+    return dequant2(gemm_wxa8_i32(A, Bp, bits), w_scale, x_scale)

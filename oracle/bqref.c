@@ -288,3 +288,30 @@ int bqref_dequant(const int32_t *acc, const uint16_t *scale, uint16_t *out,
             out[m * N + n] = bqref_f64_to_f16((double)acc[m * N + n] * bqref_f16_to_f64(scale[n]));
     return BQREF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Two-scale dequant of a linear layer with per-token activation scales     */
+/* (BMINF page, section 實現代碼分析2, PartialAttention forward: the input is */
+/* quantized per token with quantize(..., axis=1), multiplied by the int8    */
+/* weight with igemm, and each int32 result is multiplied by the scale of    */
+/* its output channel and the scale of its token, out0 = in0 * in1 * in2)   */
+/* ------------------------------------------------------------------------ */
+
+/* out[m,n] = fp16 nearest to acc[m,n] * w_scale[n] * x_scale[m] (ties to
+ * even; overflow to +-inf).  The double product is exact: |acc| < 2^31 and
+ * the two fp16 significands have 11 bits each, 31 + 11 + 11 = 53, so this is
+ * one correct rounding of the real product. */
+int bqref_dequant2(const int32_t *acc, const uint16_t *w_scale, const uint16_t *x_scale,
+                   uint16_t *out, int64_t M, int64_t N)
+{
+    if (M < 0 || N < 0)
+        return BQREF_ERR_SHAPE;
+    if (M * N > 0 && (!acc || !w_scale || !x_scale || !out))
+        return BQREF_ERR_NULL;
+    for (int64_t m = 0; m < M; ++m) {
+        const double xs = bqref_f16_to_f64(x_scale[m]);
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = bqref_f64_to_f16((double)acc[m * N + n] * bqref_f16_to_f64(w_scale[n]) * xs);
+    }
+    return BQREF_OK;
+}
