@@ -244,6 +244,46 @@ def main():
         torch.cuda.synchronize()
         big_sustained_us = g0.elapsed_time(g1) * 1e3 / reps_big
 
+    # ---------------- rows after the path, timed outside the step ----------------
+    # W8A8 linear layer with per-token activation quantization: fp16 X [64, 4096]
+    # -> int8 codes + token scales (quantize_rows), then the two-scale GEMM with
+    # the quantized fused-QKV weight [12288, 4096] (codes and scales of the step).
+    Wl, Xl = synth.bminf_linear_case(M=64)
+    del Wl
+    Xl_d = up(Xl)
+    ql = torch.empty(Xl.shape, dtype=torch.int8, device=dev)
+    sl = torch.empty((Xl.shape[0],), dtype=torch.float16, device=dev)
+    Cl = torch.empty((Xl.shape[0], W.shape[0]), dtype=torch.float16, device=dev)
+    lin_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        bq.quantize_rows(Xl_d, ql, sl)
+        bq.gemm_dual_scale(ql, q_ring[i % len(q_ring)], 8, s_ring[i % len(q_ring)], sl, Cl)
+    torch.cuda.synchronize()
+    hold_gpu()
+    for i in range(args.steps):
+        qj = i % len(q_ring)
+        lin_ev[i][0].record()
+        bq.quantize_rows(Xl_d, ql, sl)
+        lin_ev[i][1].record()
+        bq.gemm_dual_scale(ql, q_ring[qj], 8, s_ring[qj], sl, Cl)
+        lin_ev[i][2].record()
+    torch.cuda.synchronize()
+    lin_q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in lin_ev])) * 1e3
+    lin_g_us = float(np.mean([e[1].elapsed_time(e[2]) for e in lin_ev])) * 1e3
+    Ml, Kl, Nl = Xl.shape[0], Xl.shape[1], W.shape[0]
+    lin_q_bytes = roofline.quantize_bytes(Ml, Kl)
+    lin_g_bytes = roofline.gemm_bytes(Ml, Nl, Kl, 8) + 2 * Ml
+    extras = {
+        "linear_w8a8_per_token": {
+            "shape": [Ml, Nl, Kl], "path": bq.select_path(Ml, Nl, Kl, 8),
+            "quantize_us": round(lin_q_us, 2), "gemm_us": round(lin_g_us, 2),
+            "total_us": round(lin_q_us + lin_g_us, 2),
+            "GB_per_s": round((lin_q_bytes + lin_g_bytes) / ((lin_q_us + lin_g_us) * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round((lin_q_bytes + lin_g_bytes) / ((lin_q_us + lin_g_us) * 1e-6)
+                                      / roofline.HBM_PEAK_BYTES_PER_S, 4),
+        },
+    }
+
     kernel_path = {
         "quantize_rows": "quantize", "pack_int4": "pack", "pack_int2": "pack",
         "gemm_w8a8_m64": bq.select_path(64, 12288, K, 8),
@@ -342,6 +382,7 @@ def main():
             "TOPS": round(work["gemm_w4a8_m4096"]["ops"] / (big_sustained_us * 1e-6) / 1e12, 2)},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "extras": extras,
     }
     print(json.dumps(line), flush=True)
 

@@ -37,6 +37,7 @@ SIGNATURES = {
     "bq_gemm_w4a8_i32": [_P, _P, _P, _I64, _I64, _I64, _P],
     "bq_gemm_w2a8_i32": [_P, _P, _P, _I64, _I64, _I64, _P],
     "bq_gemm": [_P, _P, _I, _P, _P, _I64, _I64, _I64, _I, _P],
+    "bq_gemm_dual_scale": [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
 }
 
@@ -189,6 +190,27 @@ def gemm(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tens
     M, N, K, dev, out = _gemm_args(A, B, bits, scale, out)
     _call("bq_gemm", dev, _ptr(A), _ptr(B), bits, _ptr(scale), _ptr(out), M, N, K, _PATHS[path])
     return out
+
+
+def gemm_dual_scale(A: torch.Tensor, B: torch.Tensor, bits: int, w_scale: torch.Tensor,
+                    x_scale: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    path: str = "auto") -> torch.Tensor:
+    """fp16(acc[m,n] * w_scale[n] * x_scale[m]): the GEMM of a linear layer
+    whose M activation rows were quantized per token (codes A, scales x_scale
+    from quantize_rows)."""
+    M, N, K, dev, out = _gemm_args(A, B, bits, w_scale, out)
+    _check_tensor(x_scale, "x_scale", torch.float16, (M,), dev)
+    _call("bq_gemm_dual_scale", dev, _ptr(A), _ptr(B), bits, _ptr(w_scale), _ptr(x_scale),
+          _ptr(out), M, N, K, _PATHS[path])
+    return out
+
+
+def linear(x: torch.Tensor, B: torch.Tensor, bits: int, w_scale: torch.Tensor,
+           path: str = "auto") -> torch.Tensor:
+    """fp16 activations x [M, K] through a quantized weight: per-token int8
+    quantization of x (quantize_rows), then gemm_dual_scale."""
+    q, xs = quantize_rows(x)
+    return gemm_dual_scale(q, B, bits, w_scale, xs, path=path)
 
 
 def _named_dequant(bits, A, B, scale, out):

@@ -162,8 +162,9 @@ int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits)
     return M <= kStreamAutoMaxM ? BQ_PATH_STREAM : BQ_PATH_TILED;
 }
 
-int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,
-            int64_t M, int64_t N, int64_t K, int path, void *stream)
+static int gemm_common(const int8_t *A, const void *B, int bits, const void *scale_f16,
+                       const void *xscale_f16, void *C, int64_t M, int64_t N, int64_t K,
+                       int path, void *stream)
 {
     int st = validate_gemm(A, B, bits, scale_f16, C, M, N, K, path);
     if (st != BQ_OK || M == 0 || N == 0)
@@ -176,11 +177,29 @@ int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, voi
     const hipStream_t s = (hipStream_t)stream;
     const uint8_t *Bb = (const uint8_t *)B;
     const uint16_t *sc = (const uint16_t *)scale_f16;
+    const uint16_t *xs = (const uint16_t *)xscale_f16;
     if (path == BQ_PATH_GEMV)
-        return launch_status(bq::launch_gemv(A, Bb, bits, sc, C, (int)M, (int)N, (int)K, s));
+        return launch_status(bq::launch_gemv(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, s));
     if (path == BQ_PATH_STREAM)
-        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, C, (int)M, (int)N, (int)K, s));
-    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, C, (int)M, (int)N, (int)K, s));
+        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, s));
+    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, s));
+}
+
+int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,
+            int64_t M, int64_t N, int64_t K, int path, void *stream)
+{
+    return gemm_common(A, B, bits, scale_f16, nullptr, C, M, N, K, path, stream);
+}
+
+int bq_gemm_dual_scale(const int8_t *A, const void *B, int bits, const void *w_scale_f16,
+                       const void *x_scale_f16, void *C_f16, int64_t M, int64_t N, int64_t K,
+                       int path, void *stream)
+{
+    if (M > 0 && N > 0 && (!w_scale_f16 || !x_scale_f16))
+        return BQ_ERR_NULL;
+    if (x_scale_f16 && !aligned16(x_scale_f16))
+        return BQ_ERR_ALIGN;
+    return gemm_common(A, B, bits, w_scale_f16, x_scale_f16, C_f16, M, N, K, path, stream);
 }
 
 int bq_gemm_w8a8_dequant(const int8_t *A, const int8_t *B, const void *scale_f16,

@@ -27,16 +27,19 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 
+// The GEMM launchers: scale == nullptr selects the int32 output; with an fp16
+// output, xscale (nullable) holds a per-row activation scale [M] that
+// multiplies the weight scale.
 // Decode GEMV on the dot-product ALUs, M <= 4.
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
-                       void *C, int M, int N, int K, hipStream_t s);
-// Streaming skinny-M GEMM, M <= 64.  scale == nullptr selects int32 output.
+                       const uint16_t *xscale, void *C, int M, int N, int K, hipStream_t s);
+// Streaming skinny-M GEMM, M <= 64.
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
-                              const uint16_t *scale, void *C,
+                              const uint16_t *scale, const uint16_t *xscale, void *C,
                               int M, int N, int K, hipStream_t s);
 // LDS-tiled matrix-core GEMM, any M.
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
-                             const uint16_t *scale, void *C,
+                             const uint16_t *scale, const uint16_t *xscale, void *C,
                              int M, int N, int K, hipStream_t s);
 
 }  // namespace bq

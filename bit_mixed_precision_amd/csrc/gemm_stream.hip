@@ -39,7 +39,8 @@ __device__ __forceinline__ uint4 load16(const uint8_t *p) { return load_nt16(p);
 template <int BITS, int MT, int NT, bool F16OUT>
 __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
-    const uint16_t *__restrict__ scale, void *__restrict__ C, int M, int N, int K)
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
+    int M, int N, int K)
 {
     using U = Unpack<BITS>;
     constexpr int kValsPerLane = 32 * 8 / BITS;    // k values in a lane's 32 bytes
@@ -154,7 +155,11 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
             v >>= U::kShift;  // exact: the sum is a multiple of 2^kShift
             if (m < M && n < N) {
                 if (F16OUT) {
-                    const float s = __half2float(__ushort_as_half(scale[n]));
+                    // weight scale, times the row's activation scale when given
+                    // (a product of two fp16 values: exact in fp32)
+                    float s = __half2float(__ushort_as_half(scale[n]));
+                    if (xscale)
+                        s *= __half2float(__ushort_as_half(xscale[m]));
                     ((__half *)C)[(int64_t)m * N + n] = __float2half_rn((float)v * s);
                 } else {
                     ((int *)C)[(int64_t)m * N + n] = v;
@@ -165,40 +170,40 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
 }
 
 template <int BITS, int MT, int NT>
-hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
-                    int M, int N, int K, hipStream_t s)
+hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+                    void *C, int M, int N, int K, hipStream_t s)
 {
     const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)));
     if (scale)
-        gemm_stream_kernel<BITS, MT, NT, true><<<grid, kThreads, 0, s>>>(A, B, scale, C, M, N, K);
+        gemm_stream_kernel<BITS, MT, NT, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K);
     else
-        gemm_stream_kernel<BITS, MT, NT, false><<<grid, kThreads, 0, s>>>(A, B, scale, C, M, N, K);
+        gemm_stream_kernel<BITS, MT, NT, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K);
     return hipGetLastError();
 }
 
 template <int BITS>
-hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
-                       int M, int N, int K, hipStream_t s)
+hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+                       void *C, int M, int N, int K, hipStream_t s)
 {
     if (M <= 16)
-        return launch_t<BITS, 1, 1>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 1, 1>(A, B, scale, xscale, C, M, N, K, s);
     if (M <= 32)
-        return launch_t<BITS, 2, 2>(A, B, scale, C, M, N, K, s);
-    return launch_t<BITS, 4, 2>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 2, 2>(A, B, scale, xscale, C, M, N, K, s);
+    return launch_t<BITS, 4, 2>(A, B, scale, xscale, C, M, N, K, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
-                              const uint16_t *scale, void *C, int M, int N, int K,
-                              hipStream_t s)
+                              const uint16_t *scale, const uint16_t *xscale, void *C,
+                              int M, int N, int K, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, C, M, N, K, s);
-    case 4: return launch_bits<4>(A, B, scale, C, M, N, K, s);
-    default: return launch_bits<2>(A, B, scale, C, M, N, K, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, s);
+    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, s);
     }
 }
 

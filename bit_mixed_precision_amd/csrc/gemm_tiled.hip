@@ -155,11 +155,11 @@ struct TiledCfg {
     static_assert(kFN >= 1 && kFM >= 1 && (kFM == 1 || kFM % 2 == 0), "wave tile");
 };
 
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES>
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool XS>
 __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
-    const uint16_t *__restrict__ scale, void *__restrict__ C, int M, int N, int K,
-    int tilesM, int tilesN)
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
+    int M, int N, int K, int tilesM, int tilesN)
 {
     using U = Unpack<BITS>;
     using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES>;
@@ -336,6 +336,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // The lane's 4 x kFN groups of 4 consecutive scales for the fp16
     // epilogue, loaded before the K loop so their latency is hidden by it.
     uint2 sc[F16OUT ? T::kFN : 1][4];
+    // with XS, the activation scale of each of the lane's kFM rows
+    float xsv[XS ? T::kFM : 1];
+    if constexpr (XS) {
+#pragma unroll
+        for (int i = 0; i < T::kFM; ++i) {
+            const int m = m0 + wm * T::kWM + i * 32 + fr;
+            xsv[i] = m < M ? __half2float(__ushort_as_half(xscale[m])) : 0.0f;
+        }
+    }
     if constexpr (F16OUT) {
         const bool vecS = (N % 8) == 0;
 #pragma unroll
@@ -532,12 +541,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                     for (int ii = 0; ii < kFragsPerPass; ++ii) {
                         const int i = i0 + ii;
+                        // weight scale, times the row's activation scale with
+                        // XS (a product of two fp16 values, exact in fp32)
+                        float t[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            t[e] = XS ? s[e] * xsv[i] : s[e];
                         // pairs built as a two-element fp16 vector, so each
                         // value is one fused multiply-convert into its half
-                        const h2v p01 = {(_Float16)((float)acc[i][j][4 * g + 0] * s[0]),
-                                         (_Float16)((float)acc[i][j][4 * g + 1] * s[1])};
-                        const h2v p23 = {(_Float16)((float)acc[i][j][4 * g + 2] * s[2]),
-                                         (_Float16)((float)acc[i][j][4 * g + 3] * s[3])};
+                        const h2v p01 = {(_Float16)((float)acc[i][j][4 * g + 0] * t[0]),
+                                         (_Float16)((float)acc[i][j][4 * g + 1] * t[1])};
+                        const h2v p23 = {(_Float16)((float)acc[i][j][4 * g + 2] * t[2]),
+                                         (_Float16)((float)acc[i][j][4 * g + 3] * t[3])};
                         const int r = ii * 32 + fr;
                         *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) =
                             make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
@@ -601,25 +616,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 }
 
 template <int BITS, int BM, int BN, int STAGES, int WAVES>
-hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
-                    int M, int N, int K, hipStream_t s)
+hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+                    void *C, int M, int N, int K, hipStream_t s)
 {
     const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tilesM * tilesN));
     const bool tail = (K % kBK) != 0;
-#define BQ_TILED_LAUNCH(F16, TAIL)                                                              \
-    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES><<<grid, 64 * WAVES, 0, s>>>(A, B, scale, C, \
-                                                                               M, N, K, tilesM, tilesN)
-    if (scale) {
+#define BQ_TILED_LAUNCH(F16, TAIL, XSC)                                                         \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, XSC><<<grid, 64 * WAVES, 0, s>>>( \
+        A, B, scale, xscale, C, M, N, K, tilesM, tilesN)
+    if (scale && xscale) {
         if (tail)
-            BQ_TILED_LAUNCH(true, true);
+            BQ_TILED_LAUNCH(true, true, true);
         else
-            BQ_TILED_LAUNCH(true, false);
+            BQ_TILED_LAUNCH(true, false, true);
+    } else if (scale) {
+        if (tail)
+            BQ_TILED_LAUNCH(true, true, false);
+        else
+            BQ_TILED_LAUNCH(true, false, false);
     } else {
         if (tail)
-            BQ_TILED_LAUNCH(false, true);
+            BQ_TILED_LAUNCH(false, true, false);
         else
-            BQ_TILED_LAUNCH(false, false);
+            BQ_TILED_LAUNCH(false, false, false);
     }
 #undef BQ_TILED_LAUNCH
     return hipGetLastError();
@@ -637,8 +657,8 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, vo
 //  * 64 x 64 with an 8-stage ring below that (12.3 us at M = 128, 12.9 us at
 //    M = 256, 15 us for W8A8 at M = 64, N = 12288; 21 us with 128 x 128).
 template <int BITS>
-hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, void *C,
-                       int M, int N, int K, hipStream_t s)
+hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+                       void *C, int M, int N, int K, hipStream_t s)
 {
     // Three LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
     constexpr int kStages256 = BITS == 8 ? 2 : 3;
@@ -646,26 +666,26 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
-        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, xscale, C, M, N, K, s);
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, C, M, N, K, s);
     if (t64 >= 512)
-        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, C, M, N, K, s);
-    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, C, M, N, K, s);
+        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, C, M, N, K, s);
+    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, C, M, N, K, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
-                             const uint16_t *scale, void *C, int M, int N, int K,
-                             hipStream_t s)
+                             const uint16_t *scale, const uint16_t *xscale, void *C,
+                             int M, int N, int K, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, C, M, N, K, s);
-    case 4: return launch_bits<4>(A, B, scale, C, M, N, K, s);
-    default: return launch_bits<2>(A, B, scale, C, M, N, K, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, s);
+    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, s);
     }
 }
 

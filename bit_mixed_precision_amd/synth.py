@@ -89,6 +89,15 @@ def bminf_weight(rows: int = 3 * 4096, cols: int = 4096, seed: int = 0, std: flo
     return fp16_normal(rng(seed), (rows, cols), std)
 
 
+def bminf_linear_case(M: int = 64, rows: int = 3 * 4096, cols: int = 4096, seed: int = 0):
+    """fp16 weight [rows, cols] ~ N(0, 0.02), then fp16 activations [M, cols]
+    ~ N(0, 1) (the hidden state a linear layer quantizes per token)."""
+    g = rng(seed)
+    W = fp16_normal(g, (rows, cols), 0.02)
+    X = fp16_normal(g, (M, cols), 1.0)
+    return W, X
+
+
 def bminf_case(M: int = 64, rows: int = 3 * 4096, cols: int = 4096, seed: int = 0):
     """fp16 weight [rows, cols] ~ N(0, 0.02), then int8 activations [M, cols]."""
     g = rng(seed)

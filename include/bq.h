@@ -171,6 +171,30 @@ int bq_gemm_w2a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16,
             void *C, int64_t M, int64_t N, int64_t K, int path, void *stream);
 
+/*
+ * bq_gemm_dual_scale - the GEMM of a linear layer whose activations were
+ * quantized per token: A [M, K] holds the int8 codes of the M token rows
+ * (bq_quantize_rows over the rows of the fp16 activations) and x_scale_f16
+ * [M] their scales; then
+ *   C[m,n] = fp16(acc[m,n] * w_scale[n] * x_scale[m])
+ * (BMINF page, section 實現代碼分析2, PartialAttention forward: the input is
+ * quantized per token, multiplied by the int8 weight, and the int32 result
+ * is scaled by the weight scale of its output channel and the scale of its
+ * token, out0 = in0 * in1 * in2; reading: the product is rounded once to
+ * fp16, the kernels multiplying the two scales exactly in fp32 and rounding
+ * the product with the accumulator before the final conversion, within one
+ * fp16 ulp of the correctly rounded value).
+ *
+ *   bits, B, path   as for bq_gemm
+ *   w_scale_f16     [N] fp16 weight scales (required)
+ *   x_scale_f16     [M] fp16 token scales (required, 16-byte aligned)
+ *   C_f16           fp16 [M, N]
+ * Errors as for bq_gemm; a NULL scale gives BQ_ERR_NULL.
+ */
+int bq_gemm_dual_scale(const int8_t *A, const void *B, int bits, const void *w_scale_f16,
+                       const void *x_scale_f16, void *C_f16, int64_t M, int64_t N, int64_t K,
+                       int path, void *stream);
+
 /* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_GEMV,
  * BQ_PATH_STREAM or BQ_PATH_TILED).  Host-only integer logic; no device call. */
 int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits);

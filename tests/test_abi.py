@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -93,6 +93,20 @@ def test_gemm_validation(bq):
     assert L.bq_gemm(NULL, NULL, 8, NULL, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm(NULL, NULL, 4, NULL, NULL, 4, 0, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm_w2a8_i32(NULL, NULL, NULL, 0, 0, 0, S) == bq.BQ_OK
+
+
+def test_dual_scale_validation(bq):
+    L = bq.lib()
+    S = NULL
+    # both scales are required; the token scale must be aligned
+    assert L.bq_gemm_dual_scale(P16, P16b, 8, NULL, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm_dual_scale(P16, P16b, 8, P16c, NULL, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm_dual_scale(P16, P16b, 8, P16c, PODD, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    # the shared checks of bq_gemm apply
+    assert L.bq_gemm_dual_scale(P16, P16b, 3, P16c, P16c, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ARG
+    assert L.bq_gemm_dual_scale(P16, P16b, 8, P16c, P16c, P16d, 4, 4, 96, 0, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_gemm_dual_scale(P16, P16b, 8, P16c, P16c, PODD, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm_dual_scale(NULL, NULL, 8, NULL, NULL, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
 
 
 def test_quantize_and_pack_validation(bq):
