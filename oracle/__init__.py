@@ -247,3 +247,27 @@ def gemm_wxa8_dequant(A, Bp, scale, bits: int) -> np.ndarray:
 def gemm_wxa8_dequant2(A, Bp, w_scale, x_scale, bits: int) -> np.ndarray:
     """Steps unpack -> integer GEMM -> two-scale dequant; fp16 bits [M, N]."""
     return dequant2(gemm_wxa8_i32(A, Bp, bits), w_scale, x_scale)
+
+
+def gemm_batched(A, Bp, bits: int, scale=None, x_scale=None) -> np.ndarray:
+    """Batched form of the path: for each batch z, unpack -> integer GEMM of
+    A (shared [M, K], or A[z] of [batch, M, K]) with B[z] ([batch, N, K*bits/8])
+    -> int32 [batch, M, N], or with scale [batch, N] the fp16 bits of the
+    one-scale (or, with x_scale [M], two-scale) epilogue.
+
+    BMINF page, section 實現代碼分析2: igemm of the fused QKV weight (3, N, K)
+    with one activation (1, M, K) broadcast over the three weights."""
+    A = np.asarray(A)
+    Bp = np.asarray(Bp)
+    batch = Bp.shape[0]
+    out = []
+    for z in range(batch):
+        Az = A if A.ndim == 2 else A[z]
+        acc = gemm_wxa8_i32(np.ascontiguousarray(Az), np.ascontiguousarray(Bp[z]), bits)
+        if scale is None:
+            out.append(acc)
+        elif x_scale is None:
+            out.append(dequant(acc, np.asarray(scale)[z]))
+        else:
+            out.append(dequant2(acc, np.asarray(scale)[z], x_scale))
+    return np.stack(out)
