@@ -273,7 +273,30 @@ def main():
     Ml, Kl, Nl = Xl.shape[0], Xl.shape[1], W.shape[0]
     lin_q_bytes = roofline.quantize_bytes(Ml, Kl)
     lin_g_bytes = roofline.gemm_bytes(Ml, Nl, Kl, 8) + 2 * Ml
+    # Batched fused-QKV GEMM: the three [4096, 4096] int8 weights of the same
+    # quantized [12288, 4096] matrix in one launch, the M = 64 per-token codes
+    # broadcast to all three, two-scale epilogue.
+    Cq = torch.empty((3, Xl.shape[0], 4096), dtype=torch.float16, device=dev)
+    qkv_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        bq.gemm_batched(ql, q_ring[i % len(q_ring)].view(3, 4096, Kl), 8,
+                        s_ring[i % len(q_ring)].view(3, 4096), sl, out=Cq)
+    torch.cuda.synchronize()
+    hold_gpu()
+    for i in range(args.steps):
+        qj = i % len(q_ring)
+        qkv_ev[i][0].record()
+        bq.gemm_batched(ql, q_ring[qj].view(3, 4096, Kl), 8, s_ring[qj].view(3, 4096), sl, out=Cq)
+        qkv_ev[i][1].record()
+    torch.cuda.synchronize()
+    qkv_us = float(np.mean([e[0].elapsed_time(e[1]) for e in qkv_ev])) * 1e3
+    qkv_bytes = roofline.gemm_bytes(Ml, Nl, Kl, 8) + 2 * Ml  # A once, the three weights, scales, C
     extras = {
+        "qkv_batched_w8a8": {
+            "shape": [3, Ml, 4096, Kl], "path": bq.select_path(Ml, 4096, Kl, 8), "us": round(qkv_us, 2),
+            "GB_per_s": round(qkv_bytes / (qkv_us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(qkv_bytes / (qkv_us * 1e-6) / roofline.HBM_PEAK_BYTES_PER_S, 4),
+        },
         "linear_w8a8_per_token": {
             "shape": [Ml, Nl, Kl], "path": bq.select_path(Ml, Nl, Kl, 8),
             "quantize_us": round(lin_q_us, 2), "gemm_us": round(lin_g_us, 2),

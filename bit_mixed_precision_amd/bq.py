@@ -38,6 +38,7 @@ SIGNATURES = {
     "bq_gemm_w2a8_i32": [_P, _P, _P, _I64, _I64, _I64, _P],
     "bq_gemm": [_P, _P, _I, _P, _P, _I64, _I64, _I64, _I, _P],
     "bq_gemm_dual_scale": [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I, _P],
+    "bq_gemm_batched": [_P, _I64, _P, _I64, _I, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
 }
 
@@ -211,6 +212,38 @@ def linear(x: torch.Tensor, B: torch.Tensor, bits: int, w_scale: torch.Tensor,
     quantization of x (quantize_rows), then gemm_dual_scale."""
     q, xs = quantize_rows(x)
     return gemm_dual_scale(q, B, bits, w_scale, xs, path=path)
+
+
+def gemm_batched(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tensor] = None,
+                 x_scale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 path: str = "auto") -> torch.Tensor:
+    """Batched GEMM in one launch: B [batch, N, K*bits/8]; A [M, K] shared by
+    every batch (broadcast, the fused-QKV shape) or [batch, M, K]; scale
+    [batch, N] for the fp16 output (times x_scale [M], shared, when given),
+    else int32.  Returns [batch, M, N]."""
+    if bits not in (8, 4, 2):
+        raise ValueError("bits must be 8, 4 or 2")
+    if B.dim() != 3 or A.dim() not in (2, 3):
+        raise ValueError("B must be [batch, N, K*bits/8] and A [M, K] or [batch, M, K]")
+    batch, N, Kb = B.shape
+    M, K = A.shape[-2:]
+    dev = A.device
+    _check_tensor(A, "A", torch.int8, (M, K) if A.dim() == 2 else (batch, M, K), dev)
+    _check_tensor(B, "B", torch.int8 if bits == 8 else torch.uint8, (batch, N, K * bits // 8), dev)
+    if scale is not None:
+        _check_tensor(scale, "scale", torch.float16, (batch, N), dev)
+    if x_scale is not None:
+        if scale is None:
+            raise ValueError("x_scale needs scale")
+        _check_tensor(x_scale, "x_scale", torch.float16, (M,), dev)
+    odt = torch.float16 if scale is not None else torch.int32
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=odt, device=dev)
+    _check_tensor(out, "out", odt, (batch, M, N), dev)
+    strideA = 0 if A.dim() == 2 else M * K
+    _call("bq_gemm_batched", dev, _ptr(A), strideA, _ptr(B), N * Kb, bits, _ptr(scale),
+          N if scale is not None else 0, _ptr(x_scale), _ptr(out), M * N, batch, M, N, K, _PATHS[path])
+    return out
 
 
 def _named_dequant(bits, A, B, scale, out):

@@ -164,7 +164,7 @@ int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits)
 
 static int gemm_common(const int8_t *A, const void *B, int bits, const void *scale_f16,
                        const void *xscale_f16, void *C, int64_t M, int64_t N, int64_t K,
-                       int path, void *stream)
+                       int path, void *stream, int batch = 1, const bq::BatchStrides &bs = {})
 {
     int st = validate_gemm(A, B, bits, scale_f16, C, M, N, K, path);
     if (st != BQ_OK || M == 0 || N == 0)
@@ -179,16 +179,53 @@ static int gemm_common(const int8_t *A, const void *B, int bits, const void *sca
     const uint16_t *sc = (const uint16_t *)scale_f16;
     const uint16_t *xs = (const uint16_t *)xscale_f16;
     if (path == BQ_PATH_GEMV)
-        return launch_status(bq::launch_gemv(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, s));
+        return launch_status(bq::launch_gemv(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, batch, bs, s));
     if (path == BQ_PATH_STREAM)
-        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, s));
-    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, s));
+        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, batch, bs, s));
+    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, batch, bs, s));
 }
 
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,
             int64_t M, int64_t N, int64_t K, int path, void *stream)
 {
     return gemm_common(A, B, bits, scale_f16, nullptr, C, M, N, K, path, stream);
+}
+
+// Largest batch of bq_gemm_batched (the grid's y dimension).
+constexpr int64_t kMaxBatch = 65535;
+
+int bq_gemm_batched(const int8_t *A, int64_t strideA, const void *B, int64_t strideB, int bits,
+                    const void *scale_f16, int64_t strideScale, const void *x_scale_f16,
+                    void *C, int64_t strideC, int64_t batch, int64_t M, int64_t N, int64_t K,
+                    int path, void *stream)
+{
+    if (batch < 0 || batch > kMaxBatch || strideA < 0 || strideB < 0 || strideScale < 0 || strideC < 0 ||
+        M < 0 || N < 0)
+        return BQ_ERR_SHAPE;
+    // an empty batch is a no-op like M = 0 or N = 0 (arguments other than
+    // pointers still checked)
+    int st = validate_gemm(A, B, bits, scale_f16, C, batch == 0 ? 0 : M, N, K, path);
+    if (st != BQ_OK || batch == 0 || M == 0 || N == 0)
+        return st;
+    // outputs of different batches must not overlap; inputs may (stride 0
+    // broadcasts one operand to every batch)
+    if (batch > 1 && strideC < M * N)
+        return BQ_ERR_SHAPE;
+    if (x_scale_f16 && !scale_f16)
+        return BQ_ERR_NULL;
+    if (x_scale_f16 && !aligned16(x_scale_f16))
+        return BQ_ERR_ALIGN;
+    // every batch's operands start 16-byte aligned
+    const int64_t outBytes = scale_f16 ? 2 : 4;
+    if ((strideA % 16) != 0 || (strideB % 16) != 0 || ((strideScale * 2) % 16) != 0 ||
+        ((strideC * outBytes) % 16) != 0)
+        return BQ_ERR_ALIGN;
+    bq::BatchStrides bs;
+    bs.a = strideA;
+    bs.b = strideB;
+    bs.s = strideScale;
+    bs.c = strideC;
+    return gemm_common(A, B, bits, scale_f16, x_scale_f16, C, M, N, K, path, stream, (int)batch, bs);
 }
 
 int bq_gemm_dual_scale(const int8_t *A, const void *B, int bits, const void *w_scale_f16,

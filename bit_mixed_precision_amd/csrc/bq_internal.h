@@ -27,19 +27,27 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 
+// Per-batch element strides of a batched GEMM launch (grid dimension y is the
+// batch index z): batch z uses A + z*a, B + z*b (bytes of packed B),
+// scale + z*s and C + z*c (elements of the output type).  The activation
+// scale, when given, is shared by all batches.
+struct BatchStrides {
+    int64_t a = 0, b = 0, s = 0, c = 0;
+};
+
 // The GEMM launchers: scale == nullptr selects the int32 output; with an fp16
 // output, xscale (nullable) holds a per-row activation scale [M] that
 // multiplies the weight scale.
 // Decode GEMV on the dot-product ALUs, M <= 4.
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
-                       const uint16_t *xscale, void *C, int M, int N, int K, hipStream_t s);
+                       const uint16_t *xscale, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
 // Streaming skinny-M GEMM, M <= 64.
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
                               const uint16_t *scale, const uint16_t *xscale, void *C,
-                              int M, int N, int K, hipStream_t s);
+                              int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
 // LDS-tiled matrix-core GEMM, any M.
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
                              const uint16_t *scale, const uint16_t *xscale, void *C,
-                             int M, int N, int K, hipStream_t s);
+                             int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
 
 }  // namespace bq

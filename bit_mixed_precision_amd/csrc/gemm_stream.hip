@@ -40,8 +40,19 @@ template <int BITS, int MT, int NT, bool F16OUT>
 __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
-    int M, int N, int K)
+    int M, int N, int K, BatchStrides bs)
 {
+    if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
+        const int64_t z = blockIdx.y;
+        A += z * bs.a;
+        B += z * bs.b;
+        if (F16OUT) {
+            scale += z * bs.s;
+            C = (uint16_t *)C + z * bs.c;
+        } else {
+            C = (int *)C + z * bs.c;
+        }
+    }
     using U = Unpack<BITS>;
     constexpr int kValsPerLane = 32 * 8 / BITS;    // k values in a lane's 32 bytes
     constexpr int kMfmaPerIt = kValsPerLane / 16;  // 16 k per operand
@@ -171,39 +182,39 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
 
 template <int BITS, int MT, int NT>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                    void *C, int M, int N, int K, hipStream_t s)
+                    void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
-    const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)));
+    const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)batch);
     if (scale)
-        gemm_stream_kernel<BITS, MT, NT, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K);
+        gemm_stream_kernel<BITS, MT, NT, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
     else
-        gemm_stream_kernel<BITS, MT, NT, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K);
+        gemm_stream_kernel<BITS, MT, NT, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
     return hipGetLastError();
 }
 
 template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                       void *C, int M, int N, int K, hipStream_t s)
+                       void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M <= 16)
-        return launch_t<BITS, 1, 1>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 1, 1>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     if (M <= 32)
-        return launch_t<BITS, 2, 2>(A, B, scale, xscale, C, M, N, K, s);
-    return launch_t<BITS, 4, 2>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 2, 2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 4, 2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
                               const uint16_t *scale, const uint16_t *xscale, void *C,
-                              int M, int N, int K, hipStream_t s)
+                              int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, s);
-    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     }
 }
 

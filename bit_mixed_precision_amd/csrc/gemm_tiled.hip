@@ -159,8 +159,19 @@ template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAV
 __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
-    int M, int N, int K, int tilesM, int tilesN)
+    int M, int N, int K, int tilesM, int tilesN, BatchStrides bs)
 {
+    if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
+        const int64_t z = blockIdx.y;
+        A += z * bs.a;
+        B += z * bs.b;
+        if (F16OUT) {
+            scale += z * bs.s;
+            C = (uint16_t *)C + z * bs.c;
+        } else {
+            C = (int *)C + z * bs.c;
+        }
+    }
     using U = Unpack<BITS>;
     using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES>;
     constexpr int kThreads = T::kThreads;
@@ -617,14 +628,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 
 template <int BITS, int BM, int BN, int STAGES, int WAVES>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                    void *C, int M, int N, int K, hipStream_t s)
+                    void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tilesM * tilesN));
+    const dim3 grid((unsigned)(tilesM * tilesN), (unsigned)batch);
     const bool tail = (K % kBK) != 0;
 #define BQ_TILED_LAUNCH(F16, TAIL, XSC)                                                         \
     gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, XSC><<<grid, 64 * WAVES, 0, s>>>( \
-        A, B, scale, xscale, C, M, N, K, tilesM, tilesN)
+        A, B, scale, xscale, C, M, N, K, tilesM, tilesN, bs)
     if (scale && xscale) {
         if (tail)
             BQ_TILED_LAUNCH(true, true, true);
@@ -658,7 +669,7 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
 //    M = 256, 15 us for W8A8 at M = 64, N = 12288; 21 us with 128 x 128).
 template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                       void *C, int M, int N, int K, hipStream_t s)
+                       void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     // Three LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
     constexpr int kStages256 = BITS == 8 ? 2 : 3;
@@ -666,26 +677,26 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
-        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     if (t64 >= 512)
-        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, C, M, N, K, s);
-    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
                              const uint16_t *scale, const uint16_t *xscale, void *C,
-                             int M, int N, int K, hipStream_t s)
+                             int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, s);
-    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     }
 }
 

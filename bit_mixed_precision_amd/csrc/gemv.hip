@@ -40,8 +40,19 @@ template <int BITS, int MR, int ROWS, int U, bool F16OUT>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
-    int M, int N, int K)
+    int M, int N, int K, BatchStrides bs)
 {
+    if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
+        const int64_t z = blockIdx.y;
+        A += z * bs.a;
+        B += z * bs.b;
+        if (F16OUT) {
+            scale += z * bs.s;
+            C = (uint16_t *)C + z * bs.c;
+        } else {
+            C = (int *)C + z * bs.c;
+        }
+    }
     using Up = Unpack<BITS>;
     constexpr int kAPerChunk = 16 * 8 / BITS;  // bytes of A (= k values) per packed chunk
     const int lane = threadIdx.x & 63;
@@ -130,42 +141,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 
 template <int BITS, int MR, int ROWS, int U>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                    void *C, int M, int N, int K, hipStream_t s)
+                    void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     const int waves = (N + ROWS - 1) / ROWS;
-    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves), (unsigned)batch);
     if (scale)
-        gemv_kernel<BITS, MR, ROWS, U, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K);
+        gemv_kernel<BITS, MR, ROWS, U, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
     else
-        gemv_kernel<BITS, MR, ROWS, U, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K);
+        gemv_kernel<BITS, MR, ROWS, U, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
     return hipGetLastError();
 }
 
 template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                       void *C, int M, int N, int K, hipStream_t s)
+                       void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     // a lane's loads per batch: 2 rows x U chunks of B (64 B of packed B per
     // row at U = 4 / 2 / 1 for 8 / 4 / 2 bits: one batch covers K = 4096)
     constexpr int U = BITS == 8 ? 4 : BITS == 4 ? 2 : 1;
     if (M == 1)
-        return launch_t<BITS, 1, 2, U>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 1, 2, U>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     if (M == 2)
-        return launch_t<BITS, 2, 2, U>(A, B, scale, xscale, C, M, N, K, s);
-    return launch_t<BITS, 4, 2, U>(A, B, scale, xscale, C, M, N, K, s);
+        return launch_t<BITS, 2, 2, U>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 4, 2, U>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
-                       const uint16_t *xscale, void *C, int M, int N, int K, hipStream_t s)
+                       const uint16_t *xscale, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, s);
-    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
     }
 }
 

@@ -195,6 +195,30 @@ int bq_gemm_dual_scale(const int8_t *A, const void *B, int bits, const void *w_s
                        const void *x_scale_f16, void *C_f16, int64_t M, int64_t N, int64_t K,
                        int path, void *stream);
 
+/*
+ * bq_gemm_batched - `batch` GEMMs of one shape in one launch, batch z on
+ *   A + z*strideA, B + z*strideB, scale + z*strideScale, C + z*strideC
+ * (BMINF page, section 實現代碼分析2: igemm of the fused QKV weight
+ * (3, N, K) with the activation (1, M, K), broadcast over the 3 weights,
+ * into (3, M, N); then the two-scale elementwise step with the token scale
+ * shared by the 3 results).
+ *
+ *   strides    in elements of each array: int8 elements of A, bytes of
+ *              (packed) B, fp16 elements of scale, output elements of C.
+ *              0 broadcasts an input to every batch; strideC >= M*N when
+ *              batch > 1 (outputs must not overlap).  strideA and strideB
+ *              multiples of 16, strideScale and an fp16 strideC multiples
+ *              of 8, an int32 strideC a multiple of 4 (BQ_ERR_ALIGN).
+ *   x_scale_f16  NULL, or [M] fp16 token scales shared by every batch
+ *              (requires scale_f16; then C = fp16(acc * scale * x_scale))
+ *   batch      0 .. 65535
+ * Other arguments and errors as for bq_gemm.
+ */
+int bq_gemm_batched(const int8_t *A, int64_t strideA, const void *B, int64_t strideB, int bits,
+                    const void *scale_f16, int64_t strideScale, const void *x_scale_f16,
+                    void *C, int64_t strideC, int64_t batch, int64_t M, int64_t N, int64_t K,
+                    int path, void *stream);
+
 /* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_GEMV,
  * BQ_PATH_STREAM or BQ_PATH_TILED).  Host-only integer logic; no device call. */
 int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits);
