@@ -61,6 +61,7 @@ def _load():
             "bqref_gemm_i32": [P, P, P, I64, I64, I64],
             "bqref_dequant": [P, P, P, I64, I64],
             "bqref_dequant2": [P, P, P, P, I64, I64],
+            "bqref_dequant_act": [P, P, P, ctypes.c_int, P, I64, I64],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -73,6 +74,8 @@ def _load():
         lib.bqref_f16_to_f64_array.restype = None
         lib.bqref_f64_to_f16_array.argtypes = [P, I64, P]
         lib.bqref_f64_to_f16_array.restype = None
+        lib.bqref_act.argtypes = [ctypes.c_double, ctypes.c_int]
+        lib.bqref_act.restype = ctypes.c_double
         _lib = lib
     return _lib
 
@@ -219,6 +222,36 @@ def dequant2(acc, w_scale, x_scale) -> np.ndarray:
     out = np.empty((M, N), np.uint16)
     _check(_load().bqref_dequant2(_ptr(acc), _ptr(w_scale), _ptr(x_scale), _ptr(out), M, N),
            "dequant2")
+    return out
+
+
+ACTS = {"none": 0, "relu": 1, "gelu": 2}
+
+
+def act(v: float, name: str) -> float:
+    """The epilogue activation in double: identity, ReLU, or GELU
+    v * Phi(v) with Phi(v) = erfc(-v / sqrt(2)) / 2."""
+    return _load().bqref_act(float(v), ACTS[name])
+
+
+def dequant_act(acc, w_scale, x_scale, name: str) -> np.ndarray:
+    """fp16(act(acc[m,n] * w_scale[n] * x_scale[m])) rounded once (x_scale
+    None = 1); uint16 bits.  JAX Pallas matmul page, fused-activation section:
+    the activation on the wide result of the last K step, one downcast."""
+    acc = _c(acc, np.int32)
+    w_scale = _bits16(w_scale)
+    M, N = acc.shape
+    if w_scale.shape != (N,):
+        raise ValueError("w_scale must be [N]")
+    xp = None
+    if x_scale is not None:
+        x_scale = _bits16(x_scale)
+        if x_scale.shape != (M,):
+            raise ValueError("x_scale must be [M]")
+        xp = _ptr(x_scale)
+    out = np.empty((M, N), np.uint16)
+    _check(_load().bqref_dequant_act(_ptr(acc), _ptr(w_scale), xp, ACTS[name], _ptr(out), M, N),
+           "dequant_act")
     return out
 
 

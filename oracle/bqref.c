@@ -315,3 +315,45 @@ int bqref_dequant2(const int32_t *acc, const uint16_t *w_scale, const uint16_t *
     }
     return BQREF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Activation fused into the epilogue (JAX Pallas matmul page, fused-        */
+/* activation section: the activation is applied once, to the wide           */
+/* accumulated result of the last K step, before the single downcast;       */
+/* BladeDISC page, CUTLASS GEMM codegen: GEMM followed by GELU fused)       */
+/* ------------------------------------------------------------------------ */
+
+/* act 0: identity; 1: ReLU max(v, 0); 2: GELU v * Phi(v) with the standard
+ * normal CDF Phi(v) = erfc(-v / sqrt(2)) / 2 (the complementary form has no
+ * cancellation for negative v). */
+double bqref_act(double v, int act)
+{
+    if (act == 1)
+        return v > 0.0 ? v : 0.0;
+    if (act == 2)
+        return 0.5 * v * erfc(-v / sqrt(2.0));
+    return v;
+}
+
+/* out[m,n] = fp16 nearest to act(acc[m,n] * w_scale[n] * x_scale[m]) with
+ * x_scale NULL meaning 1.  The product is exact in double (see dequant2);
+ * ReLU keeps it exact; GELU is evaluated in double (libm erfc) and rounded
+ * once to fp16. */
+int bqref_dequant_act(const int32_t *acc, const uint16_t *w_scale, const uint16_t *x_scale,
+                      int act, uint16_t *out, int64_t M, int64_t N)
+{
+    if (M < 0 || N < 0)
+        return BQREF_ERR_SHAPE;
+    if (act < 0 || act > 2)
+        return BQREF_ERR_RANGE;
+    if (M * N > 0 && (!acc || !w_scale || !out))
+        return BQREF_ERR_NULL;
+    for (int64_t m = 0; m < M; ++m) {
+        const double xs = x_scale ? bqref_f16_to_f64(x_scale[m]) : 1.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double v = (double)acc[m * N + n] * bqref_f16_to_f64(w_scale[n]) * xs;
+            out[m * N + n] = bqref_f64_to_f16(bqref_act(v, act));
+        }
+    }
+    return BQREF_OK;
+}
