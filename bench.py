@@ -291,7 +291,28 @@ def main():
     torch.cuda.synchronize()
     qkv_us = float(np.mean([e[0].elapsed_time(e[1]) for e in qkv_ev])) * 1e3
     qkv_bytes = roofline.gemm_bytes(Ml, Nl, Kl, 8) + 2 * Ml  # A once, the three weights, scales, C
+    # The M = 4096 W4A8 GEMM with GELU fused into the epilogue (the Pallas
+    # page's fused-activation experiment: utilization with the activation
+    # against without it, the plain launch being the step's).
+    act_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        bq.gemm_act(A4096_d, B4p_ring[i % len(B4p_ring)], 4, s4_d, None, act="gelu", out=C4096)
+    torch.cuda.synchronize()
+    hold_gpu()
+    for i in range(args.steps):
+        pj = (i + len(B4p_ring) // 2) % len(B4p_ring)
+        act_ev[i][0].record()
+        bq.gemm_act(A4096_d, B4p_ring[pj], 4, s4_d, None, act="gelu", out=C4096)
+        act_ev[i][1].record()
+    torch.cuda.synchronize()
+    gelu_us = float(np.mean([e[0].elapsed_time(e[1]) for e in act_ev])) * 1e3
+
     extras = {
+        "gemm_w4a8_m4096_gelu": {
+            "shape": [4096, 4096, 4096], "us": round(gelu_us, 2),
+            "TOPS": round(roofline.gemm_ops(4096, 4096, K) / (gelu_us * 1e-6) / 1e12, 2),
+            "vs_plain_epilogue": round(mean_ms[names.index("gemm_w4a8_m4096")] * 1e3 / gelu_us, 4),
+        },
         "qkv_batched_w8a8": {
             "shape": [3, Ml, 4096, Kl], "path": bq.select_path(Ml, 4096, Kl, 8), "us": round(qkv_us, 2),
             "GB_per_s": round(qkv_bytes / (qkv_us * 1e-6) / 1e9, 1),

@@ -39,6 +39,7 @@ SIGNATURES = {
     "bq_gemm": [_P, _P, _I, _P, _P, _I64, _I64, _I64, _I, _P],
     "bq_gemm_dual_scale": [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I, _P],
     "bq_gemm_batched": [_P, _I64, _P, _I64, _I, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P],
+    "bq_gemm_act": [_P, _P, _I, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
 }
 
@@ -206,12 +207,33 @@ def gemm_dual_scale(A: torch.Tensor, B: torch.Tensor, bits: int, w_scale: torch.
     return out
 
 
+ACTS = {"none": 0, "relu": 1, "gelu": 2}
+
+
+def gemm_act(A: torch.Tensor, B: torch.Tensor, bits: int, w_scale: torch.Tensor,
+             x_scale: Optional[torch.Tensor] = None, act: str = "gelu",
+             out: Optional[torch.Tensor] = None, path: str = "auto") -> torch.Tensor:
+    """fp16(act(acc[m,n] * w_scale[n] * x_scale[m])) with act "none", "relu"
+    or "gelu" fused into the epilogue (x_scale None = 1)."""
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {sorted(ACTS)}")
+    M, N, K, dev, out = _gemm_args(A, B, bits, w_scale, out)
+    if x_scale is not None:
+        _check_tensor(x_scale, "x_scale", torch.float16, (M,), dev)
+    _call("bq_gemm_act", dev, _ptr(A), _ptr(B), bits, _ptr(w_scale), _ptr(x_scale), ACTS[act],
+          _ptr(out), M, N, K, _PATHS[path])
+    return out
+
+
 def linear(x: torch.Tensor, B: torch.Tensor, bits: int, w_scale: torch.Tensor,
-           path: str = "auto") -> torch.Tensor:
+           act: str = "none", path: str = "auto") -> torch.Tensor:
     """fp16 activations x [M, K] through a quantized weight: per-token int8
-    quantization of x (quantize_rows), then gemm_dual_scale."""
+    quantization of x (quantize_rows), then the two-scale GEMM with the
+    activation act fused."""
     q, xs = quantize_rows(x)
-    return gemm_dual_scale(q, B, bits, w_scale, xs, path=path)
+    if act == "none":
+        return gemm_dual_scale(q, B, bits, w_scale, xs, path=path)
+    return gemm_act(q, B, bits, w_scale, xs, act=act, path=path)
 
 
 def gemm_batched(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tensor] = None,

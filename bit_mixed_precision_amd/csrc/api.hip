@@ -163,7 +163,7 @@ int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits)
 }
 
 static int gemm_common(const int8_t *A, const void *B, int bits, const void *scale_f16,
-                       const void *xscale_f16, void *C, int64_t M, int64_t N, int64_t K,
+                       const void *xscale_f16, int act, void *C, int64_t M, int64_t N, int64_t K,
                        int path, void *stream, int batch = 1, const bq::BatchStrides &bs = {})
 {
     int st = validate_gemm(A, B, bits, scale_f16, C, M, N, K, path);
@@ -179,16 +179,16 @@ static int gemm_common(const int8_t *A, const void *B, int bits, const void *sca
     const uint16_t *sc = (const uint16_t *)scale_f16;
     const uint16_t *xs = (const uint16_t *)xscale_f16;
     if (path == BQ_PATH_GEMV)
-        return launch_status(bq::launch_gemv(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, batch, bs, s));
+        return launch_status(bq::launch_gemv(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s));
     if (path == BQ_PATH_STREAM)
-        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, batch, bs, s));
-    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, xs, C, (int)M, (int)N, (int)K, batch, bs, s));
+        return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s));
+    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s));
 }
 
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,
             int64_t M, int64_t N, int64_t K, int path, void *stream)
 {
-    return gemm_common(A, B, bits, scale_f16, nullptr, C, M, N, K, path, stream);
+    return gemm_common(A, B, bits, scale_f16, nullptr, 0, C, M, N, K, path, stream);
 }
 
 // Largest batch of bq_gemm_batched (the grid's y dimension).
@@ -225,7 +225,7 @@ int bq_gemm_batched(const int8_t *A, int64_t strideA, const void *B, int64_t str
     bs.b = strideB;
     bs.s = strideScale;
     bs.c = strideC;
-    return gemm_common(A, B, bits, scale_f16, x_scale_f16, C, M, N, K, path, stream, (int)batch, bs);
+    return gemm_common(A, B, bits, scale_f16, x_scale_f16, 0, C, M, N, K, path, stream, (int)batch, bs);
 }
 
 int bq_gemm_dual_scale(const int8_t *A, const void *B, int bits, const void *w_scale_f16,
@@ -236,7 +236,20 @@ int bq_gemm_dual_scale(const int8_t *A, const void *B, int bits, const void *w_s
         return BQ_ERR_NULL;
     if (x_scale_f16 && !aligned16(x_scale_f16))
         return BQ_ERR_ALIGN;
-    return gemm_common(A, B, bits, w_scale_f16, x_scale_f16, C_f16, M, N, K, path, stream);
+    return gemm_common(A, B, bits, w_scale_f16, x_scale_f16, 0, C_f16, M, N, K, path, stream);
+}
+
+int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f16,
+                const void *x_scale_f16, int act, void *C_f16, int64_t M, int64_t N, int64_t K,
+                int path, void *stream)
+{
+    if (act != BQ_ACT_NONE && act != BQ_ACT_RELU && act != BQ_ACT_GELU)
+        return BQ_ERR_ARG;
+    if (M > 0 && N > 0 && !w_scale_f16)
+        return BQ_ERR_NULL;
+    if (x_scale_f16 && !aligned16(x_scale_f16))
+        return BQ_ERR_ALIGN;
+    return gemm_common(A, B, bits, w_scale_f16, x_scale_f16, act, C_f16, M, N, K, path, stream);
 }
 
 int bq_gemm_w8a8_dequant(const int8_t *A, const int8_t *B, const void *scale_f16,

@@ -27,6 +27,18 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 
+// Activation applied to the dequantized fp32 value before the fp16
+// conversion: 0 identity, 1 ReLU, 2 GELU v * Phi(v) with the standard normal
+// CDF Phi(v) = erfc(-v / sqrt(2)) / 2 (no cancellation for negative v).
+__device__ __forceinline__ float apply_act(float v, int act)
+{
+    if (act == 1)
+        return fmaxf(v, 0.0f);
+    if (act == 2)
+        return 0.5f * v * erfcf(-v * 0.70710678118654752f);
+    return v;
+}
+
 // Per-batch element strides of a batched GEMM launch (grid dimension y is the
 // batch index z): batch z uses A + z*a, B + z*b (bytes of packed B),
 // scale + z*s and C + z*c (elements of the output type).  The activation
@@ -37,17 +49,18 @@ struct BatchStrides {
 
 // The GEMM launchers: scale == nullptr selects the int32 output; with an fp16
 // output, xscale (nullable) holds a per-row activation scale [M] that
-// multiplies the weight scale.
+// multiplies the weight scale, and act (apply_act) is applied before the
+// conversion.
 // Decode GEMV on the dot-product ALUs, M <= 4.
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
-                       const uint16_t *xscale, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
+                       const uint16_t *xscale, int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
 // Streaming skinny-M GEMM, M <= 64.
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
-                              const uint16_t *scale, const uint16_t *xscale, void *C,
+                              const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                               int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
 // LDS-tiled matrix-core GEMM, any M.
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
-                             const uint16_t *scale, const uint16_t *xscale, void *C,
+                             const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                              int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
 
 }  // namespace bq

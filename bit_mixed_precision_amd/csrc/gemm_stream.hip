@@ -39,7 +39,8 @@ __device__ __forceinline__ uint4 load16(const uint8_t *p) { return load_nt16(p);
 template <int BITS, int MT, int NT, bool F16OUT>
 __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
-    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, int act,
+    void *__restrict__ C,
     int M, int N, int K, BatchStrides bs)
 {
     if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
                     float s = __half2float(__ushort_as_half(scale[n]));
                     if (xscale)
                         s *= __half2float(__ushort_as_half(xscale[m]));
-                    ((__half *)C)[(int64_t)m * N + n] = __float2half_rn((float)v * s);
+                    ((__half *)C)[(int64_t)m * N + n] = __float2half_rn(apply_act((float)v * s, act));
                 } else {
                     ((int *)C)[(int64_t)m * N + n] = v;
                 }
@@ -181,40 +182,40 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(
 }
 
 template <int BITS, int MT, int NT>
-hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale, int act,
                     void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)batch);
     if (scale)
-        gemm_stream_kernel<BITS, MT, NT, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
+        gemm_stream_kernel<BITS, MT, NT, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, act, C, M, N, K, bs);
     else
-        gemm_stream_kernel<BITS, MT, NT, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
+        gemm_stream_kernel<BITS, MT, NT, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, act, C, M, N, K, bs);
     return hipGetLastError();
 }
 
 template <int BITS>
-hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale, int act,
                        void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M <= 16)
-        return launch_t<BITS, 1, 1>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 1, 1>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (M <= 32)
-        return launch_t<BITS, 2, 2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    return launch_t<BITS, 4, 2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 2, 2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 4, 2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
-                              const uint16_t *scale, const uint16_t *xscale, void *C,
+                              const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                               int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    default: return launch_bits<2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     }
 }
 

@@ -155,10 +155,12 @@ struct TiledCfg {
     static_assert(kFN >= 1 && kFM >= 1 && (kFM == 1 || kFM % 2 == 0), "wave tile");
 };
 
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool XS>
+// FUSE: fp16 epilogue with the optional per-row activation scale (xscale,
+// NULL meaning 1) and the activation act; the plain fp16 epilogue has none.
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE>
 __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
-    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, int act, void *__restrict__ C,
     int M, int N, int K, int tilesM, int tilesN, BatchStrides bs)
 {
     if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
@@ -347,13 +349,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // The lane's 4 x kFN groups of 4 consecutive scales for the fp16
     // epilogue, loaded before the K loop so their latency is hidden by it.
     uint2 sc[F16OUT ? T::kFN : 1][4];
-    // with XS, the activation scale of each of the lane's kFM rows
-    float xsv[XS ? T::kFM : 1];
-    if constexpr (XS) {
+    // with FUSE, the activation scale of each of the lane's kFM rows
+    float xsv[FUSE ? T::kFM : 1];
+    if constexpr (FUSE) {
 #pragma unroll
         for (int i = 0; i < T::kFM; ++i) {
             const int m = m0 + wm * T::kWM + i * 32 + fr;
-            xsv[i] = m < M ? __half2float(__ushort_as_half(xscale[m])) : 0.0f;
+            xsv[i] = !xscale ? 1.0f : m < M ? __half2float(__ushort_as_half(xscale[m])) : 0.0f;
         }
     }
     if constexpr (F16OUT) {
@@ -553,17 +555,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                     for (int ii = 0; ii < kFragsPerPass; ++ii) {
                         const int i = i0 + ii;
                         // weight scale, times the row's activation scale with
-                        // XS (a product of two fp16 values, exact in fp32)
-                        float t[4];
+                        // FUSE (a product of two fp16 values, exact in fp32),
+                        // then the activation
+                        float v[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            t[e] = XS ? s[e] * xsv[i] : s[e];
-                        // pairs built as a two-element fp16 vector, so each
-                        // value is one fused multiply-convert into its half
-                        const h2v p01 = {(_Float16)((float)acc[i][j][4 * g + 0] * t[0]),
-                                         (_Float16)((float)acc[i][j][4 * g + 1] * t[1])};
-                        const h2v p23 = {(_Float16)((float)acc[i][j][4 * g + 2] * t[2]),
-                                         (_Float16)((float)acc[i][j][4 * g + 3] * t[3])};
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? s[e] * xsv[i] : s[e]);
+                            if constexpr (FUSE)
+                                v[e] = apply_act(v[e], act);
+                        }
+                        // pairs converted as two-element fp16 vectors
+                        const h2v p01 = {(_Float16)v[0], (_Float16)v[1]};
+                        const h2v p23 = {(_Float16)v[2], (_Float16)v[3]};
                         const int r = ii * 32 + fr;
                         *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) =
                             make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
@@ -628,15 +631,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 
 template <int BITS, int BM, int BN, int STAGES, int WAVES>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                    void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
+                    int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tilesM * tilesN), (unsigned)batch);
     const bool tail = (K % kBK) != 0;
-#define BQ_TILED_LAUNCH(F16, TAIL, XSC)                                                         \
-    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, XSC><<<grid, 64 * WAVES, 0, s>>>( \
-        A, B, scale, xscale, C, M, N, K, tilesM, tilesN, bs)
-    if (scale && xscale) {
+#define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                       \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED><<<grid, 64 * WAVES, 0, s>>>( \
+        A, B, scale, xscale, act, C, M, N, K, tilesM, tilesN, bs)
+    if (scale && (xscale || act != 0)) {
         if (tail)
             BQ_TILED_LAUNCH(true, true, true);
         else
@@ -669,7 +672,7 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
 //    M = 256, 15 us for W8A8 at M = 64, N = 12288; 21 us with 128 x 128).
 template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                       void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
+                       int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     // Three LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
     constexpr int kStages256 = BITS == 8 ? 2 : 3;
@@ -677,26 +680,26 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
-        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (t64 >= 512)
-        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
-                             const uint16_t *scale, const uint16_t *xscale, void *C,
+                             const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                              int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    default: return launch_bits<2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     }
 }
 

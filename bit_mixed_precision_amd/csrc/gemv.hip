@@ -39,7 +39,8 @@ __device__ __forceinline__ int wave_sum(int v)
 template <int BITS, int MR, int ROWS, int U, bool F16OUT>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
-    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, void *__restrict__ C,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, int act,
+    void *__restrict__ C,
     int M, int N, int K, BatchStrides bs)
 {
     if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                     float sc = __half2float(__ushort_as_half(scale[n]));
                     if (xscale)
                         sc *= __half2float(__ushort_as_half(xscale[m]));
-                    ((__half *)C)[(int64_t)m * N + n] = __float2half_rn((float)v * sc);
+                    ((__half *)C)[(int64_t)m * N + n] = __float2half_rn(apply_act((float)v * sc, act));
                 } else
                     ((int *)C)[(int64_t)m * N + n] = v;
             }
@@ -140,43 +141,43 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 }
 
 template <int BITS, int MR, int ROWS, int U>
-hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale, int act,
                     void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     const int waves = (N + ROWS - 1) / ROWS;
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves), (unsigned)batch);
     if (scale)
-        gemv_kernel<BITS, MR, ROWS, U, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
+        gemv_kernel<BITS, MR, ROWS, U, true><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, act, C, M, N, K, bs);
     else
-        gemv_kernel<BITS, MR, ROWS, U, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, C, M, N, K, bs);
+        gemv_kernel<BITS, MR, ROWS, U, false><<<grid, kThreads, 0, s>>>(A, B, scale, xscale, act, C, M, N, K, bs);
     return hipGetLastError();
 }
 
 template <int BITS>
-hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
+hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale, int act,
                        void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     // a lane's loads per batch: 2 rows x U chunks of B (64 B of packed B per
     // row at U = 4 / 2 / 1 for 8 / 4 / 2 bits: one batch covers K = 4096)
     constexpr int U = BITS == 8 ? 4 : BITS == 4 ? 2 : 1;
     if (M == 1)
-        return launch_t<BITS, 1, 2, U>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 1, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (M == 2)
-        return launch_t<BITS, 2, 2, U>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    return launch_t<BITS, 4, 2, U>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 2, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 4, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
-                       const uint16_t *xscale, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
+                       const uint16_t *xscale, int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
-    default: return launch_bits<2>(A, B, scale, xscale, C, M, N, K, batch, bs, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 4: return launch_bits<4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    default: return launch_bits<2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     }
 }
 

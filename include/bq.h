@@ -219,6 +219,33 @@ int bq_gemm_batched(const int8_t *A, int64_t strideA, const void *B, int64_t str
                     void *C, int64_t strideC, int64_t batch, int64_t M, int64_t N, int64_t K,
                     int path, void *stream);
 
+/* Activation of the fused epilogue (bq_gemm_act). */
+enum bq_act {
+    BQ_ACT_NONE = 0, /* identity                                               */
+    BQ_ACT_RELU = 1, /* max(v, 0)                                              */
+    BQ_ACT_GELU = 2  /* v * Phi(v), Phi the standard normal CDF                */
+};
+
+/*
+ * bq_gemm_act - the GEMM with an activation fused into the fp16 epilogue:
+ *   C[m,n] = fp16(act(acc[m,n] * w_scale[n] * x_scale[m]))
+ * with x_scale NULL meaning 1 (JAX Pallas matmul page, fused-activation
+ * section: the activation is applied once to the wide result of the last K
+ * step, before the single downcast; BladeDISC page, CUTLASS GEMM codegen:
+ * GEMM + GELU fused).  Reading: the activation acts on the dequantized value;
+ * the kernels evaluate it in fp32 (GELU as v * erfc(-v / sqrt(2)) / 2) and
+ * round once to fp16; outputs within one fp16 ulp of the correctly rounded
+ * value.
+ *
+ *   act          enum bq_act (BQ_ERR_ARG otherwise)
+ *   w_scale_f16  [N] fp16 (required)
+ *   x_scale_f16  [M] fp16 token scales, or NULL (16-byte aligned)
+ * Other arguments and errors as for bq_gemm.
+ */
+int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f16,
+                const void *x_scale_f16, int act, void *C_f16, int64_t M, int64_t N, int64_t K,
+                int path, void *stream);
+
 /* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_GEMV,
  * BQ_PATH_STREAM or BQ_PATH_TILED).  Host-only integer logic; no device call. */
 int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits);

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -93,6 +93,17 @@ def test_gemm_validation(bq):
     assert L.bq_gemm(NULL, NULL, 8, NULL, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm(NULL, NULL, 4, NULL, NULL, 4, 0, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm_w2a8_i32(NULL, NULL, NULL, 0, 0, 0, S) == bq.BQ_OK
+
+
+def test_act_validation(bq):
+    L = bq.lib()
+    S = NULL
+    assert L.bq_gemm_act(P16, P16b, 8, P16c, NULL, 3, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ARG
+    assert L.bq_gemm_act(P16, P16b, 8, P16c, NULL, -1, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ARG
+    assert L.bq_gemm_act(P16, P16b, 8, NULL, NULL, 2, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm_act(P16, P16b, 8, P16c, PODD, 2, P16d, 4, 4, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm_act(P16, P16b, 8, P16c, NULL, 1, P16d, 4, 4, 96, 0, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_gemm_act(NULL, NULL, 8, NULL, NULL, 2, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
 
 
 def test_dual_scale_validation(bq):
