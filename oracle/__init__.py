@@ -54,6 +54,7 @@ def _load():
         I64 = ctypes.c_int64
         for name, args in {
             "bqref_quantize_rows": [P, I64, I64, P, P],
+            "bqref_quantize_rows_q": [P, I64, I64, ctypes.c_int, P, P],
             "bqref_pack_int4": [P, I64, I64, P],
             "bqref_unpack_int4": [P, I64, I64, P],
             "bqref_pack_int2": [P, I64, I64, P],
@@ -142,6 +143,24 @@ def quantize_rows(x) -> tuple[np.ndarray, np.ndarray]:
     s = np.empty((rows,), np.uint16)
     _check(_load().bqref_quantize_rows(_ptr(x), rows, cols, _ptr(q), _ptr(s)),
            "quantize_rows")
+    return q, s
+
+
+def quantize_rows_bits(x, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row symmetric quantization to the code range of `bits` (8, 4, 2):
+    qmax = 2^(bits-1) - 1, scale = fp16(absmax/qmax), codes = nearest integer
+    of x/scale clamped to [-qmax, qmax]; the BMINF page's int8 rule with the
+    code range of the packed formats."""
+    if bits not in (8, 4, 2):
+        raise ValueError("bits must be 8, 4 or 2")
+    x = _bits16(x)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows,), np.uint16)
+    _check(_load().bqref_quantize_rows_q(_ptr(x), rows, cols, (1 << (bits - 1)) - 1, _ptr(q), _ptr(s)),
+           "quantize_rows_bits")
     return q, s
 
 

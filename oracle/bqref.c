@@ -102,26 +102,30 @@ void bqref_f64_to_f16_array(const double *d, int64_t n, uint16_t *out)
 /* Step 1+2: per-row symmetric int8 quantization (BMINF page)               */
 /* ------------------------------------------------------------------------ */
 
-/* For each row r of x [rows, cols] (fp16, row-major):
+/* For each row r of x [rows, cols] (fp16, row-major) and a code range
+ * qmax (127 for int8 as on the BMINF page; 7 and 1 give the int4 and
+ * ternary code ranges, qmax = 2^(bits-1) - 1):
  *   amax_r  = max_k |x[r,k]|                      (exact)
- *   scale_r = fp16 nearest to amax_r / 127         (ties to even)
+ *   scale_r = fp16 nearest to amax_r / qmax        (ties to even)
  *   q[r,k]  = nearest integer to x[r,k] / scale_r  (ties to even),
- *             clamped to [-127, 127]
+ *             clamped to [-qmax, qmax]
  * A row whose scale rounds to zero (all zeros, or amax at most 63 * 2^-24)
  * gets scale 0 and codes 0.
  *
- * Exactness of the double arithmetic used here: amax/127 and x/scale are
+ * Exactness of the double arithmetic used here: amax/qmax and x/scale are
  * quotients of fp16 values; neither can fall within double precision of a
  * rounding midpoint of the target format (fp16 resp. the half-integers)
  * without being exactly on it, because both operands carry at most 11
  * significant bits while the target grid is at least 2^-13 relative apart
  * from any such quotient; so rounding the double quotient once more gives
  * the correctly rounded result of the exact quotient. */
-int bqref_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
-                        int8_t *q, uint16_t *scale)
+int bqref_quantize_rows_q(const uint16_t *x, int64_t rows, int64_t cols, int qmax,
+                          int8_t *q, uint16_t *scale)
 {
     if (rows < 0 || cols < 0)
         return BQREF_ERR_SHAPE;
+    if (qmax < 1 || qmax > 127)
+        return BQREF_ERR_RANGE;
     if (rows > 0 && (!scale || (cols > 0 && (!x || !q))))
         return BQREF_ERR_NULL;
     int status = BQREF_OK;
@@ -142,22 +146,29 @@ int bqref_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
             status = BQREF_ERR_RANGE;
             continue;
         }
-        uint16_t s16 = bqref_f64_to_f16(amax / 127.0);
+        uint16_t s16 = bqref_f64_to_f16(amax / (double)qmax);
         double s = bqref_f16_to_f64(s16);
         scale[r] = s16;
         for (int64_t k = 0; k < cols; ++k) {
             double c = 0.0;
             if (s != 0.0) {
                 c = nearbyint(bqref_f16_to_f64(xr[k]) / s);
-                if (c > 127.0)
-                    c = 127.0;
-                if (c < -127.0)
-                    c = -127.0;
+                if (c > qmax)
+                    c = qmax;
+                if (c < -qmax)
+                    c = -qmax;
             }
             q[r * cols + k] = (int8_t)c;
         }
     }
     return status;
+}
+
+/* The int8 form of the BMINF page (qmax = 127). */
+int bqref_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
+                        int8_t *q, uint16_t *scale)
+{
+    return bqref_quantize_rows_q(x, rows, cols, 127, q, scale);
 }
 
 /* ------------------------------------------------------------------------ */
