@@ -307,7 +307,35 @@ def main():
     torch.cuda.synchronize()
     gelu_us = float(np.mean([e[0].elapsed_time(e[1]) for e in act_ev])) * 1e3
 
+    # int4 weight preparation from fp16: the fused-QKV weight [12288, 4096]
+    # quantized to the int4 code range, then packed (two launches).
+    q4 = torch.empty(W.shape, dtype=torch.int8, device=dev)
+    s4q = torch.empty((W.shape[0],), dtype=torch.float16, device=dev)
+    p4 = torch.empty((W.shape[0], W.shape[1] // 2), dtype=torch.uint8, device=dev)
+    prep_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        bq.quantize_rows_bits(W_d[i % len(W_d)], 4, q4, s4q)
+        bq.pack_int4(q4, p4)
+    torch.cuda.synchronize()
+    hold_gpu()
+    for i in range(args.steps):
+        prep_ev[i][0].record()
+        bq.quantize_rows_bits(W_d[i % len(W_d)], 4, q4, s4q)
+        prep_ev[i][1].record()
+        bq.pack_int4(q4, p4)
+        prep_ev[i][2].record()
+    torch.cuda.synchronize()
+    prep_q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in prep_ev])) * 1e3
+    prep_p_us = float(np.mean([e[1].elapsed_time(e[2]) for e in prep_ev])) * 1e3
+    prep_bytes = roofline.quantize_bytes(*W.shape) + roofline.pack_bytes(W.shape[0], W.shape[1], 4)
+
     extras = {
+        "weight_prep_int4": {
+            "shape": list(W.shape), "quantize_us": round(prep_q_us, 2), "pack_us": round(prep_p_us, 2),
+            "GB_per_s": round(prep_bytes / ((prep_q_us + prep_p_us) * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(prep_bytes / ((prep_q_us + prep_p_us) * 1e-6)
+                                      / roofline.HBM_PEAK_BYTES_PER_S, 4),
+        },
         "gemm_w4a8_m4096_gelu": {
             "shape": [4096, 4096, 4096], "us": round(gelu_us, 2),
             "TOPS": round(roofline.gemm_ops(4096, 4096, K) / (gelu_us * 1e-6) / 1e12, 2),

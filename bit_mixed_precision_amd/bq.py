@@ -40,6 +40,7 @@ SIGNATURES = {
     "bq_gemm_dual_scale": [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I, _P],
     "bq_gemm_batched": [_P, _I64, _P, _I64, _I, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P],
     "bq_gemm_act": [_P, _P, _I, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P],
+    "bq_quantize_rows_bits": [_P, _I64, _I64, _I, _P, _P, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
 }
 
@@ -136,6 +137,28 @@ def quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     _check_tensor(q, "q", torch.int8, (rows, cols), dev)
     _check_tensor(scale, "scale", torch.float16, (rows,), dev)
     _call("bq_quantize_rows", dev, _ptr(x), rows, cols, _ptr(q), _ptr(scale))
+    return q, scale
+
+
+def quantize_rows_bits(x: torch.Tensor, bits: int, q: Optional[torch.Tensor] = None,
+                       scale: Optional[torch.Tensor] = None):
+    """Per-row quantization of fp16 x [rows, cols] to the code range of a
+    weight format, qmax = 2^(bits-1) - 1 (bits 8, 4, 2) -> (q int8, scale fp16
+    [rows]); the codes feed pack_int4 / pack_int2."""
+    if bits not in (8, 4, 2):
+        raise ValueError("bits must be 8, 4 or 2")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    _check_tensor(x, "x", torch.float16)
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float16, device=dev)
+    _check_tensor(q, "q", torch.int8, (rows, cols), dev)
+    _check_tensor(scale, "scale", torch.float16, (rows,), dev)
+    _call("bq_quantize_rows_bits", dev, _ptr(x), rows, cols, bits, _ptr(q), _ptr(scale))
     return q, scale
 
 

@@ -105,8 +105,8 @@ const char *bq_status_string(int status)
     }
 }
 
-int bq_quantize_rows(const void *x_f16, int64_t rows, int64_t cols, int8_t *q,
-                     void *scale_f16, void *stream)
+static int quantize_common(const void *x_f16, int64_t rows, int64_t cols, int qmax, int8_t *q,
+                           void *scale_f16, void *stream)
 {
     if (rows < 0 || cols < 0 || rows > INT32_MAX)
         return BQ_ERR_SHAPE;
@@ -119,8 +119,22 @@ int bq_quantize_rows(const void *x_f16, int64_t rows, int64_t cols, int8_t *q,
     const int dev = check_device();
     if (dev != BQ_OK)
         return dev;
-    return launch_status(bq::launch_quantize_rows((const uint16_t *)x_f16, rows, cols, q,
+    return launch_status(bq::launch_quantize_rows((const uint16_t *)x_f16, rows, cols, qmax, q,
                                                   (uint16_t *)scale_f16, (hipStream_t)stream));
+}
+
+int bq_quantize_rows(const void *x_f16, int64_t rows, int64_t cols, int8_t *q,
+                     void *scale_f16, void *stream)
+{
+    return quantize_common(x_f16, rows, cols, 127, q, scale_f16, stream);
+}
+
+int bq_quantize_rows_bits(const void *x_f16, int64_t rows, int64_t cols, int bits, int8_t *q,
+                          void *scale_f16, void *stream)
+{
+    if (bits != 8 && bits != 4 && bits != 2)
+        return BQ_ERR_ARG;
+    return quantize_common(x_f16, rows, cols, (1 << (bits - 1)) - 1, q, scale_f16, stream);
 }
 
 static int pack_common(const int8_t *v, int64_t n, int64_t k, uint8_t *out, int factor)

@@ -22,7 +22,8 @@ __device__ __forceinline__ uint4 load_nt16(const void *p)
 // Kernel launchers.  Arguments have been validated by the C ABI layer:
 // sizes are non-negative and within limits, pointers non-null and aligned.
 // Each returns the status of the launch (hipGetLastError after it).
-hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
+// Codes in [-qmax, qmax], scale = fp16(absmax / qmax); 1 <= qmax <= 127.
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int qmax,
                                 int8_t *q, uint16_t *scale, hipStream_t s);
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);

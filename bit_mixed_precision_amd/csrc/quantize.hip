@@ -1,4 +1,4 @@
-// Per-row symmetric int8 quantization of an fp16 matrix.
+// Per-row symmetric quantization of an fp16 matrix to int8 codes.
 //
 // BMINF post-training quantization page ("BMINF的後訓練量化實現"), section
 // 實現代碼分析2: the quantize() docstring runs two kernels, a per-row
@@ -8,8 +8,11 @@
 // (wavefront shuffles, then LDS across the four wavefronts) and writes the
 // codes, so x is read from HBM once.
 //
+// The code range is [-qmax, qmax]: qmax = 127 for int8 as on the page, and
+// qmax = 2^(bits-1) - 1 = 7 or 1 for the int4 and ternary weight formats.
+//
 // Rounding: the code is the nearest integer to the EXACT quotient x/scale,
-// ties to even, clamped to [-127, 127].  Without a division per element:
+// ties to even, clamped to [-qmax, qmax].  Without a division per element:
 //   q0 = rint(x * r), r = 1/scale rounded to fp32.
 // x and scale are fp16 values (11 significant bits), so a quotient that is
 // not exactly a half-integer lies at least 2^-13 from every half-integer,
@@ -17,10 +20,11 @@
 // an exact half-integer (a tie) the residual e = x - q0*scale, computed
 // exactly by one fma (q0*scale has at most 19 significant bits), equals
 // +-scale/2, and q0 is moved to the even neighbour if it is odd.
-// The scale itself is fp16(absmax / 127): fp32 division rounded once more
-// to fp16 equals the correctly rounded quotient for every fp16 absmax (the
-// quotient has a repeating binary expansion of period 7 unless exact, so
-// it never sits within fp32 precision of an fp16 midpoint).
+// The scale itself is fp16(absmax / qmax): fp32 division rounded once more
+// to fp16 equals the correctly rounded quotient for every fp16 absmax (a
+// quotient that is not exactly an fp16 midpoint lies at least 2^-12 / qmax
+// relative from one, far outside fp32 precision; checked exhaustively for
+// qmax = 127, 7 and 1).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -46,14 +50,14 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h)
     return __half2float(__ushort_as_half((unsigned short)h));
 }
 
-__device__ __forceinline__ int code_of(float x, float s, float r, float hs)
+__device__ __forceinline__ int code_of(float x, float s, float r, float hs, int qmax)
 {
     float q0 = __builtin_rintf(x * r);
     float e = __builtin_fmaf(-q0, s, x);
     int q = (int)q0;
     if (__builtin_fabsf(e) == hs && (q & 1))
         q += (e > 0.f) ? 1 : -1;
-    return min(max(q, -127), 127);
+    return min(max(q, -qmax), qmax);
 }
 
 // Row absmax over the workgroup; every thread gets the result.
@@ -71,13 +75,14 @@ __device__ __forceinline__ uint32_t block_absmax(uint32_t m, uint32_t *red)
 
 struct RowScale {
     float s, r, hs;
+    int qmax;
     bool zero;
 };
 
-__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits, uint16_t *scale_out)
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits, int qmax, uint16_t *scale_out)
 {
     const float a = half_bits_to_float(amax_bits);
-    const __half sh = __float2half_rn(__fdiv_rn(a, 127.0f));
+    const __half sh = __float2half_rn(__fdiv_rn(a, (float)qmax));
     if (threadIdx.x == 0)
         *scale_out = __half_as_ushort(sh);
     RowScale rs;
@@ -85,15 +90,16 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits, uint16_t *scal
     rs.zero = (rs.s == 0.0f);
     rs.r = rs.zero ? 0.0f : __fdiv_rn(1.0f, rs.s);
     rs.hs = 0.5f * rs.s;
+    rs.qmax = qmax;
     return rs;
 }
 
 __device__ __forceinline__ uint32_t codes4(uint32_t w0, uint32_t w1, const RowScale &rs)
 {
-    const int c0 = code_of(half_bits_to_float(w0 & 0xFFFF), rs.s, rs.r, rs.hs);
-    const int c1 = code_of(half_bits_to_float(w0 >> 16), rs.s, rs.r, rs.hs);
-    const int c2 = code_of(half_bits_to_float(w1 & 0xFFFF), rs.s, rs.r, rs.hs);
-    const int c3 = code_of(half_bits_to_float(w1 >> 16), rs.s, rs.r, rs.hs);
+    const int c0 = code_of(half_bits_to_float(w0 & 0xFFFF), rs.s, rs.r, rs.hs, rs.qmax);
+    const int c1 = code_of(half_bits_to_float(w0 >> 16), rs.s, rs.r, rs.hs, rs.qmax);
+    const int c2 = code_of(half_bits_to_float(w1 & 0xFFFF), rs.s, rs.r, rs.hs, rs.qmax);
+    const int c3 = code_of(half_bits_to_float(w1 >> 16), rs.s, rs.r, rs.hs, rs.qmax);
     return (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
            ((uint32_t)(c2 & 0xFF) << 16) | ((uint32_t)(c3 & 0xFF) << 24);
 }
@@ -104,7 +110,7 @@ __device__ __forceinline__ uint32_t codes4(uint32_t w0, uint32_t w1, const RowSc
 // cover rows of up to 2048*VPT elements, held in registers.
 template <int VPT>
 __global__ __launch_bounds__(kThreads) void quantize_rows_vec(
-    const uint4 *__restrict__ x, int64_t cols, uint2 *__restrict__ q,
+    const uint4 *__restrict__ x, int64_t cols, int qmax, uint2 *__restrict__ q,
     uint16_t *__restrict__ scale)
 {
     __shared__ uint32_t red[4];
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_vec(
         m2 = absmax2(m2, v[j].w);
     }
     const uint32_t amax = block_absmax(max(m2 & 0xFFFF, m2 >> 16), red);
-    const RowScale rs = row_scale(amax, scale + row);
+    const RowScale rs = row_scale(amax, qmax, scale + row);
 
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_vec(
 // General path for any cols (and rows too long for registers): two passes
 // over the row, the second normally served from L2.
 __global__ __launch_bounds__(kThreads) void quantize_rows_any(
-    const uint16_t *__restrict__ x, int64_t cols, int8_t *__restrict__ q,
+    const uint16_t *__restrict__ x, int64_t cols, int qmax, int8_t *__restrict__ q,
     uint16_t *__restrict__ scale)
 {
     __shared__ uint32_t red[4];
@@ -155,14 +161,14 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_any(
     for (int64_t k = threadIdx.x; k < cols; k += kThreads)
         m = max(m, (uint32_t)(xr[k] & 0x7FFF));
     const uint32_t amax = block_absmax(m, red);
-    const RowScale rs = row_scale(amax, scale + row);
+    const RowScale rs = row_scale(amax, qmax, scale + row);
     for (int64_t k = threadIdx.x; k < cols; k += kThreads)
-        qr[k] = rs.zero ? 0 : (int8_t)code_of(half_bits_to_float(xr[k]), rs.s, rs.r, rs.hs);
+        qr[k] = rs.zero ? 0 : (int8_t)code_of(half_bits_to_float(xr[k]), rs.s, rs.r, rs.hs, rs.qmax);
 }
 
 }  // namespace
 
-hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int qmax,
                                 int8_t *q, uint16_t *scale, hipStream_t s)
 {
     if (rows == 0)
@@ -171,15 +177,15 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols,
     const int64_t nvec = cols / 8;
     const bool vec = (cols % 8 == 0) && cols > 0;
     if (vec && nvec <= 1 * kThreads)
-        quantize_rows_vec<1><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+        quantize_rows_vec<1><<<grid, block, 0, s>>>((const uint4 *)x, cols, qmax, (uint2 *)q, scale);
     else if (vec && nvec <= 2 * kThreads)
-        quantize_rows_vec<2><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+        quantize_rows_vec<2><<<grid, block, 0, s>>>((const uint4 *)x, cols, qmax, (uint2 *)q, scale);
     else if (vec && nvec <= 4 * kThreads)
-        quantize_rows_vec<4><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+        quantize_rows_vec<4><<<grid, block, 0, s>>>((const uint4 *)x, cols, qmax, (uint2 *)q, scale);
     else if (vec && nvec <= 8 * kThreads)
-        quantize_rows_vec<8><<<grid, block, 0, s>>>((const uint4 *)x, cols, (uint2 *)q, scale);
+        quantize_rows_vec<8><<<grid, block, 0, s>>>((const uint4 *)x, cols, qmax, (uint2 *)q, scale);
     else
-        quantize_rows_any<<<grid, block, 0, s>>>(x, cols, q, scale);
+        quantize_rows_any<<<grid, block, 0, s>>>(x, cols, qmax, q, scale);
     return hipGetLastError();
 }
 

@@ -99,6 +99,18 @@ int bq_quantize_rows(const void *x_f16, int64_t rows, int64_t cols,
                      int8_t *q, void *scale_f16, void *stream);
 
 /*
+ * bq_quantize_rows_bits - bq_quantize_rows with the code range of a weight
+ * format: qmax = 2^(bits-1) - 1 (127, 7 or 1 for bits 8, 4, 2), scale_f16 =
+ * fp16(absmax_row / qmax), codes clamped to [-qmax, qmax] (the BMINF page's
+ * per-row rule, section 實現代碼分析2, with the int4 / ternary code range; the
+ * codes feed bq_pack_int4 / bq_pack_int2 directly).
+ *   bits  8, 4 or 2 (BQ_ERR_ARG otherwise); other arguments, layouts and
+ *         errors as for bq_quantize_rows.
+ */
+int bq_quantize_rows_bits(const void *x_f16, int64_t rows, int64_t cols, int bits, int8_t *q,
+                          void *scale_f16, void *stream);
+
+/*
  * bq_pack_int4 - pack int4 values held one per int8 into bytes along K.
  * BitBLAS guide, case 2 (uint8 [N, K/2] compressed storage); bit order:
  * byte [n, k/2] = (v[n,k] & 0xF) | (v[n,k+1] & 0xF) << 4 for even k.

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -93,6 +93,17 @@ def test_gemm_validation(bq):
     assert L.bq_gemm(NULL, NULL, 8, NULL, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm(NULL, NULL, 4, NULL, NULL, 4, 0, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm_w2a8_i32(NULL, NULL, NULL, 0, 0, 0, S) == bq.BQ_OK
+
+
+def test_quantize_bits_validation(bq):
+    L = bq.lib()
+    S = NULL
+    for bits in (0, 1, 3, 16):
+        assert L.bq_quantize_rows_bits(P16, 4, 64, bits, P16b, P16c, S) == bq.BQ_ERR_ARG
+    assert L.bq_quantize_rows_bits(P16, -1, 64, 4, P16b, P16c, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_quantize_rows_bits(P16, 4, 64, 4, P16b, NULL, S) == bq.BQ_ERR_NULL
+    assert L.bq_quantize_rows_bits(PODD, 4, 64, 4, P16b, P16c, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_quantize_rows_bits(NULL, 0, 64, 2, NULL, NULL, S) == bq.BQ_OK
 
 
 def test_act_validation(bq):

@@ -113,3 +113,66 @@ def test_pack_out_of_range_keeps_low_bits(dev):
     assert np.array_equal(p4, oracle.pack_int4(lo4.astype(np.int8)))
     lo2 = (((v.astype(np.int16) + 2) & 3) - 2)          # low 2 bits of v+2, as a code
     assert np.array_equal(p2, oracle.pack_int2(lo2.astype(np.int8)))
+
+
+# ---- quantization to the int4 / ternary code ranges (qmax 7 / 1) ----
+
+def _quantize_bits_case(dev, x16: np.ndarray, bits: int, what: str):
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner(f"quantize_rows_bits bits={bits} {what} shape={x16.shape}")
+    q, s = bq.quantize_rows_bits(to_dev(x16, dev), bits)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows_bits(x16, bits)
+    assert np.array_equal(f16_bits(s), s_ref), f"{what}: scales differ"
+    qg = q.cpu().numpy()
+    if not np.array_equal(qg, q_ref):
+        bad = np.argwhere(qg != q_ref)
+        r, k = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} codes differ, first at {(r, k)}: "
+                             f"x={x16[r, k]!r} got {qg[r, k]} want {q_ref[r, k]}")
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("shape", [(3, 7), (5, 8), (9, 1000), (4, 4096), (2, 16392), (300, 64)])
+def test_quantize_bits_shapes(dev, bits, shape):
+    g = np.random.default_rng(shape[0] * 7 + shape[1] + bits)
+    x = (g.standard_normal(shape) * np.exp(g.uniform(-6, 6, (shape[0], 1)))).astype(np.float16)
+    _quantize_bits_case(dev, x, bits, "random")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_quantize_bits_special_rows(dev, bits):
+    qmax = (1 << (bits - 1)) - 1
+    q = 2.0 ** -24
+    rows = np.zeros((5, 16), np.float64)
+    rows[1, :4] = [q, -q, 0, 0]                      # tiny row: the int4 scale underflows
+    rows[2, :4] = [40 * q, -40 * q, 7 * q, q]        # subnormal scale
+    s0 = 2.0 ** -3                                   # exact ties x = (n + 1/2) * s
+    rows[3, 0] = qmax * s0
+    halves = np.arange(-qmax, qmax) + 0.5
+    rows[3, 1:1 + len(halves)] = halves * s0
+    rows[4, :] = np.linspace(-65504, 65504, 16)
+    _quantize_bits_case(dev, rows.astype(np.float16), bits, "special rows")
+
+
+def test_fp16_to_int4_gemm_flow(dev):
+    """fp16 weight -> int4 codes and scales (GPU) -> pack (GPU) -> W4A8 GEMM
+    (GPU) against the oracle's same steps."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner("fp16 -> int4 -> pack -> w4a8 flow")
+    g = np.random.default_rng(77)
+    W = synth.fp16_normal(g, (1000, 1024), 0.02)
+    A = synth.int8_uniform(g, (96, 1024))
+    q, s = bq.quantize_rows_bits(to_dev(W, dev), 4)
+    Bp = bq.pack_int4(q)
+    C = bq.gemm(to_dev(A, dev), Bp, 4, s)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows_bits(W, 4)
+    assert np.array_equal(Bp.cpu().numpy(), oracle.pack_int4(q_ref))
+    ref = oracle.gemm_wxa8_dequant(A, oracle.pack_int4(q_ref), s_ref, 4)
+    from gpu_util import assert_f16_within_1ulp
+    assert_f16_within_1ulp(f16_bits(C), ref, "int4 flow")
