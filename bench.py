@@ -54,7 +54,7 @@ def parse():
 
 
 # Kernel sources of the tiled matrix-core GEMM; the committed HBM-traffic
-# summary is used only while these files are unchanged.
+# summary is used only while these files and the compiler flags are unchanged.
 TILED_SOURCES = ["gemm_tiled.hip", "unpack.h", "bq_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a8_m4096_hbm_traffic.txt")
 
@@ -62,10 +62,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a8_m4096_hbm_traffic.txt")
 def tiled_source_hash() -> str:
     import hashlib
 
+    from bit_mixed_precision_amd import _build
+
     h = hashlib.sha256()
     for f in TILED_SOURCES:
         with open(os.path.join(ROOT, "bit_mixed_precision_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
 

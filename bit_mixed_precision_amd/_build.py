@@ -20,6 +20,9 @@ FLAGS = [
     "-fPIC",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: with the accumulation
+    # registers the allocator shuffled accumulators between loop halves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -513,11 +513,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         wait_stage();
         __syncthreads();
         read_stage(0, 0);
-        for (int step = 0; step < steps; step += 2) {
+        // both halves unconditional inside the loop, so the accumulators keep
+        // their registers across it; an odd last step runs after it
+        int step = 0;
+        for (; step + 1 < steps; step += 2) {
             one_step(step, 0);
-            if (step + 1 < steps)
-                one_step(step + 1, 1);
+            one_step(step + 1, 1);
         }
+        if (step < steps)
+            one_step(step, 0);
     }
 
     // The loads issued in the last steps (zeros past K) must land before LDS
