@@ -42,6 +42,9 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <vector>
+
 #include "bq_internal.h"
 #include "unpack.h"
 
@@ -116,6 +119,18 @@ __device__ __forceinline__ void wait_vmcnt_rt(int c)
     }
 }
 
+// K split of each output tile over `parts` workgroups: workgroup q of a tile
+// runs the 128-k stages [q stepsPer, (q+1) stepsPer) and stores its int32
+// partial sums; the last of the tile's workgroups to arrive (a per-tile
+// counter) adds the others' partial sums to its own and runs the epilogue.
+// Integer addition is exact, so the result does not depend on the split.
+struct SplitK {
+    int parts = 1;           // workgroups per output tile
+    int stepsPer = 0;        // 128-k stages per workgroup
+    int *ctr = nullptr;      // per-tile arrival counters, zero between launches
+    int4 *part = nullptr;    // partial sums: [tile][part][8-byte piece][thread]
+};
+
 template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES>
 struct TiledCfg {
     static constexpr int kThreads = 64 * WAVES;
@@ -157,11 +172,12 @@ struct TiledCfg {
 
 // FUSE: fp16 epilogue with the optional per-row activation scale (xscale,
 // NULL meaning 1) and the activation act; the plain fp16 epilogue has none.
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE>
+// SPLIT: the K split above (blockIdx.x = part * tiles + tile).
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, int act, void *__restrict__ C,
-    int M, int N, int K, int tilesM, int tilesN, BatchStrides bs)
+    int M, int N, int K, int tilesM, int tilesN, BatchStrides bs, SplitK sk)
 {
     if (gridDim.y > 1) {  // batch blockIdx.y (BatchStrides)
         const int64_t z = blockIdx.y;
@@ -185,6 +201,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // ---- tile coordinates (XCD-aware) ----
     const int total = tilesM * tilesN;
     int t = blockIdx.x;
+    int split = 0;
+    if constexpr (SPLIT) {
+        split = t / total;
+        t -= split * total;
+    }
     if (total % kXcds == 0)
         t = (t % kXcds) * (total / kXcds) + t / kXcds;
     const int perGroup = kGroupM * tilesN;
@@ -202,7 +223,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int wm = wave / T::kWGN, wn = wave % T::kWGN;
 
     const uint32_t rowBytesB = (uint32_t)((int64_t)K * BITS / 8);
-    const int steps = (K + kBK - 1) / kBK;
+    // this workgroup's 128-k stages: [s0, s0 + steps) of the whole K
+    const int s0 = SPLIT ? split * sk.stepsPer : 0;
+    const int steps = SPLIT ? min((K + kBK - 1) / kBK - s0, sk.stepsPer) : (K + kBK - 1) / kBK;
 
     // Buffer resources over this tile's rows: rows past M / N are past the end.
     const v4si srcA = make_rsrc(A + (int64_t)m0 * K, (uint32_t)(min(M - m0, BM) * K));
@@ -255,7 +278,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // offset and read as zeros.
     auto issue_stage = [&](int step, int part, int nparts) {
         const uint32_t base = ldsBase + (uint32_t)((step % STAGES) * T::kStage);
-        const int sstep = min(step, steps - 1);
+        const int sstep = s0 + min(step, steps - 1);
         const int ka = sstep * kBK;
         const uint32_t kb = (uint32_t)sstep * T::kPB;
 #pragma unroll
@@ -528,6 +551,60 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // is reused or the wavefront ends.
     wait_vmcnt<0>();
 
+    if constexpr (SPLIT) {
+        // Exchange of the partial sums, coherent across the XCDs without
+        // cache-wide write-back or invalidation: the partial sums are stored
+        // and loaded as agent-scope relaxed atomics (8 bytes at a time, lane-
+        // major, coalesced), which the compiler issues with the device-scope
+        // cache policy (written through to, and read from, the level shared
+        // by all XCDs), piece q of every lane next to piece q of the next lane.
+        // Every workgroup stores its sums and waits until the
+        // stores have completed before the barrier after which one thread
+        // counts the arrival; the last of the tile's workgroups then loads
+        // the others' sums and adds them to its own.
+        constexpr int kQ = T::kFM * T::kFN * 8;  // 8-byte pieces per lane
+        const int64_t tile0 = (int64_t)t * sk.parts * kQ * kThreads + tid;
+        long long *mine = (long long *)sk.part + tile0 + (int64_t)split * kQ * kThreads;
+#pragma unroll
+        for (int i = 0; i < T::kFM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::kFN; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint64_t v = (uint32_t)acc[i][j][2 * q] | ((uint64_t)(uint32_t)acc[i][j][2 * q + 1] << 32);
+                    __hip_atomic_store(mine + ((i * T::kFN + j) * 8 + q) * kThreads, (long long)v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+        wait_vmcnt<0>();
+        __syncthreads();
+        __shared__ int lastArrival;
+        if (tid == 0) {
+            const int arrived = atomicAdd(sk.ctr + t, 1) + 1;
+            lastArrival = arrived == sk.parts;
+            if (arrived == sk.parts)
+                atomicExch(sk.ctr + t, 0);  // ready for the next launch
+        }
+        __syncthreads();
+        if (!lastArrival)
+            return;
+        for (int p = 0; p < sk.parts; ++p) {
+            if (p == split)
+                continue;
+            const long long *other = (const long long *)sk.part + tile0 + (int64_t)p * kQ * kThreads;
+#pragma unroll
+            for (int i = 0; i < T::kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint64_t v = (uint64_t)__hip_atomic_load(other + ((i * T::kFN + j) * 8 + q) * kThreads,
+                                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        acc[i][j][2 * q] += (int)(uint32_t)v;
+                        acc[i][j][2 * q + 1] += (int)(uint32_t)(v >> 32);
+                    }
+        }
+    }
+
     // ---- epilogue ----
     // Accumulator layout (C transposed): lane l of acc[i][j] holds row
     // m = wm*kWM + 32 i + (l & 31) and, in registers 4g..4g+3, the four
@@ -633,16 +710,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     }
 }
 
-template <int BITS, int BM, int BN, int STAGES, int WAVES>
+template <int BITS, int BM, int BN, int STAGES, int WAVES, bool SPLIT = false>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                    int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
+                    int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
+                    const SplitK &sk = {})
 {
     const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tilesM * tilesN), (unsigned)batch);
+    const dim3 grid((unsigned)(tilesM * tilesN * (SPLIT ? sk.parts : 1)), (unsigned)batch);
     const bool tail = (K % kBK) != 0;
-#define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                       \
-    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED><<<grid, 64 * WAVES, 0, s>>>( \
-        A, B, scale, xscale, act, C, M, N, K, tilesM, tilesN, bs)
+#define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                              \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED, SPLIT><<<grid, 64 * WAVES, 0, s>>>( \
+        A, B, scale, xscale, act, C, M, N, K, tilesM, tilesN, bs, sk)
     if (scale && (xscale || act != 0)) {
         if (tail)
             BQ_TILED_LAUNCH(true, true, true);
@@ -672,8 +750,65 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
 //  * 64 x 64, four wavefronts (32 x 32 each), a 4-stage ring, from 512 tiles
 //    (several workgroups per CU; 17 us at M = 512, against 22 us with
 //    128 x 128 tiles);
-//  * 64 x 64 with an 8-stage ring below that (12.3 us at M = 128, 12.9 us at
-//    M = 256, 15 us for W8A8 at M = 64, N = 12288; 21 us with 128 x 128).
+//  * 64 x 64 with an 8-stage ring below that (11.1 us at M = 128, 12.2 us at
+//    M = 256, 15 us for W8A8 at M = 64, N = 12288; 21 us with 128 x 128);
+//    with at most 128 such tiles (half the CUs or fewer), K is split over
+//    2-8 workgroups per tile (SplitK) so that up to 256 workgroups run
+//    (M = 64: 11.0 -> 10.0 us; M = 128: 11.1 -> 10.4 us, W2A8 14.4 -> 11.9 us,
+//    W8A8 12.5 -> 11.0 us).
+
+// Split-K workspace of one (device, stream): the per-tile counters, then the
+// partial sums.  Allocated (and the counters zeroed on the stream) at the
+// first split launch on that stream, kept until the process ends; calls on
+// one stream are ordered, so they never share it concurrently.  A stream
+// under graph capture gets none (no allocation there): it runs unsplit.
+constexpr int kSplitMaxTiles = 128;   // split only with this many tiles or fewer
+constexpr int kSplitMaxWgs = 256;     // tiles x parts
+constexpr int kSplitMaxParts = 8;
+constexpr int kSplitMinSteps = 4;     // 128-k stages per workgroup, at least
+constexpr size_t kCtrBytes = 4096;
+constexpr size_t kPartBytes = (size_t)kSplitMaxWgs * 256 * 16 * 4;  // 256 threads x 16 int32 each
+
+struct Workspace {
+    int dev;
+    hipStream_t stream;
+    void *mem;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+bool split_workspace(hipStream_t s, SplitK &sk)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return false;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void *mem = nullptr;
+    for (const Workspace &w : g_ws)
+        if (w.dev == dev && w.stream == s)
+            mem = w.mem;
+    if (!mem) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+            (void)hipGetLastError();
+            return false;
+        }
+        if (hipMalloc(&mem, kCtrBytes + kPartBytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        if (hipMemsetAsync(mem, 0, kCtrBytes, s) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(mem);
+            return false;
+        }
+        g_ws.push_back({dev, s, mem});
+    }
+    sk.ctr = (int *)mem;
+    sk.part = (int4 *)((char *)mem + kCtrBytes);
+    return true;
+}
+
 template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
                        int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
@@ -689,6 +824,17 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
         return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (t64 >= 512)
         return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    if (batch == 1 && t64 <= kSplitMaxTiles) {
+        const int stepsAll = (K + kBK - 1) / kBK;
+        int parts = min(kSplitMaxParts, min(kSplitMaxWgs / (int)t64, stepsAll / kSplitMinSteps));
+        SplitK sk;
+        if (parts >= 2 && split_workspace(s, sk)) {
+            // equal stage counts; the rounding never leaves a workgroup empty
+            sk.stepsPer = (stepsAll + parts - 1) / parts;
+            sk.parts = (stepsAll + sk.stepsPer - 1) / sk.stepsPer;
+            return launch_t<BITS, 64, 64, 8, 4, true>(A, B, scale, xscale, act, C, M, N, K, 1, bs, s, sk);
+        }
+    }
     return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
 }
 

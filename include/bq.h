@@ -39,8 +39,20 @@
  *    across the ABI.  A dimension of 0 (other than K) is a valid no-op.
  *  - The device must be gfx950 (BQ_ERR_DEVICE otherwise); the check is made
  *    once per device.
- *  - Thread safety: calls are reentrant; the only shared state is a cached
- *    per-device property record, written once.
+ *  - Library memory: a GEMM on the tiled kernel with few output tiles
+ *    (64 x 64 tiles, at most 128 of them, K >= 1024, not batched) splits K
+ *    over several workgroups per tile, which exchange int32 partial sums
+ *    through a workspace of 4 MiB + 4 KiB.  The library allocates it with
+ *    hipMalloc at the first such call on each (device, stream) and keeps it
+ *    until the process ends; calls on one stream are ordered, so they never
+ *    share it concurrently.  If the stream is being captured into a graph
+ *    and has no workspace yet, or the allocation fails, the call runs with
+ *    K unsplit (same results).  A graph captured with the split replays it
+ *    on the workspace of the stream it was captured on: do not replay it
+ *    concurrently with other work on that stream's GEMMs.
+ *  - Thread safety: calls are reentrant; the shared state is a cached
+ *    per-device property record, written once, and the workspace list
+ *    above, guarded by a mutex.
  */
 #ifndef BQ_H
 #define BQ_H

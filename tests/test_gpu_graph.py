@@ -1,8 +1,11 @@
-"""The path captured in a HIP graph (torch.cuda.graph on the current stream)
-and replayed: quantize -> pack -> GEMMs on every kernel path, with eager work
-and synchronizations between replays.  Every replay must give the eager
-results bit for bit (the kernels are deterministic), which also shows that no
-call of the path allocates, synchronizes or memsets inside the capture."""
+"""The path captured in a HIP graph (torch.cuda.graph on the stream that ran
+the warm-up) and replayed: quantize -> pack -> GEMMs on every kernel path,
+with eager work and synchronizations between replays.  Every replay must give
+the eager results bit for bit (the kernels are deterministic), which also
+shows that no call of the path allocates, synchronizes or memsets inside the
+capture.  The tiled GEMM here splits K over workgroups (16 tiles, K = 1024),
+so the graph replays the split kernel with the stream's workspace, whose
+per-tile counters must reset themselves on every replay."""
 import numpy as np
 import pytest
 
@@ -62,7 +65,7 @@ def test_graph_replays_match_eager(dev):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=s):
         path(gbuf)
     for rep in range(4):
         for v in gbuf.values():  # poison the outputs between replays
