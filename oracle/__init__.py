@@ -21,6 +21,10 @@ the order of its steps are those of the pages:
 Readings taken where the pages leave a step open are stated in the C source
 and in the design notes: round-half-even of the exact quotient, codes clamped
 to [-127, 127], zero scale -> zero codes, one correct rounding of acc*scale.
+
+The submodule ``oracle.nf4`` (plain numpy) covers the W4A16 GEMM with NF4
+weight codes, a per-row scale and zero point of the same BitBLAS guide
+(case 2); its readings are stated in its own header.
 """
 from __future__ import annotations
 
