@@ -42,6 +42,7 @@ SIGNATURES = {
     "bq_gemm_act": [_P, _P, _I, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P],
     "bq_quantize_rows_bits": [_P, _I64, _I64, _I, _P, _P, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
+    "bq_gemm_nf4_a16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P],
 }
 
 
@@ -330,3 +331,27 @@ def gemm_w4a8_i32(A, B, out=None):
 
 def gemm_w2a8_i32(A, B, out=None):
     return _named_i32(2, A, B, out)
+
+
+def gemm_nf4_a16(A: torch.Tensor, B: torch.Tensor, scale: torch.Tensor,
+                 zero: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W4A16 GEMM with NF4 weight codes: C = fp16(sum_k A[m,k] W[n,k]) with
+    W[n,k] = fp16((nf4[code] - zero[n]) * scale[n]) and fp32 accumulation.
+
+    A fp16 [M, K]; B uint8 [N, K/2] (code of k even in the low nibble);
+    scale fp16 [N]; zero fp16 [N] or None (0)."""
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N = B.shape[0]
+    dev = A.device
+    _check_tensor(A, "A", torch.float16)
+    _check_tensor(B, "B", torch.uint8, (N, K // 2), dev)
+    _check_tensor(scale, "scale", torch.float16, (N,), dev)
+    if zero is not None:
+        _check_tensor(zero, "zero", torch.float16, (N,), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _check_tensor(out, "out", torch.float16, (M, N), dev)
+    _call("bq_gemm_nf4_a16", dev, _ptr(A), _ptr(B), _ptr(scale), _ptr(zero), _ptr(out), M, N, K)
+    return out

@@ -266,6 +266,26 @@ int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f1
     return gemm_common(A, B, bits, w_scale_f16, x_scale_f16, act, C_f16, M, N, K, path, stream);
 }
 
+int bq_gemm_nf4_a16(const void *A_f16, const uint8_t *B, const void *scale_f16, const void *zero_f16,
+                    void *C_f16, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0 || K > BQ_MAX_K || (K % 64) != 0 || M > INT32_MAX || N > INT32_MAX)
+        return BQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return BQ_OK;
+    if (!C_f16 || !scale_f16 || (K > 0 && (!A_f16 || !B)))
+        return BQ_ERR_NULL;
+    if (!aligned16(C_f16) || !aligned16(scale_f16) || (zero_f16 && !aligned16(zero_f16)) ||
+        (K > 0 && (!aligned16(A_f16) || !aligned16(B))))
+        return BQ_ERR_ALIGN;
+    const int st = check_device();
+    if (st != BQ_OK)
+        return st;
+    return launch_status(bq::launch_gemm_nf4((const uint16_t *)A_f16, B, (const uint16_t *)scale_f16,
+                                             (const uint16_t *)zero_f16, (uint16_t *)C_f16, (int)M, (int)N,
+                                             (int)K, (hipStream_t)stream));
+}
+
 int bq_gemm_w8a8_dequant(const int8_t *A, const int8_t *B, const void *scale_f16,
                          void *C_f16, int64_t M, int64_t N, int64_t K, void *stream)
 {

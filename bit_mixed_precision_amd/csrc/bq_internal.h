@@ -63,5 +63,9 @@ hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
                              const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                              int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
+// W4A16 GEMM with NF4 weight codes on the tiled kernel: A fp16 [M, K], B
+// codes [N, K/2], per-row scale and zero point (zero may be NULL), C fp16.
+hipError_t launch_gemm_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero,
+                           uint16_t *C, int M, int N, int K, hipStream_t s);
 
 }  // namespace bq

@@ -46,6 +46,7 @@
 #include <vector>
 
 #include "bq_internal.h"
+#include "nf4_table.h"
 #include "unpack.h"
 
 namespace bq {
@@ -68,6 +69,43 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
 typedef int v4si __attribute__((ext_vector_type(4)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// One matrix-core step on a 32 x 32 tile: int8 x int8 -> int32 over 32 k,
+// or (NF4) fp16 x fp16 -> fp32 over 16 k; B fragment first (C transposed).
+template <bool NF4, typename Acc>
+__device__ __forceinline__ Acc mma32(const v4i &b, const v4i &a, const Acc &c)
+{
+    if constexpr (NF4)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, b), __builtin_bit_cast(v8h, a), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c, 0, 0, 0);
+}
+
+// Eight 4-bit codes (one dword, the lowest k in the low nibble) -> eight
+// fp16 weights of one B row, looked up in that row's 16-entry table in LDS.
+__device__ __forceinline__ v4i decode_nf4(uint32_t p, const uint16_t *row)
+{
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = row[(p >> (8 * e)) & 15u];
+        const uint32_t hi = row[(p >> (8 * e + 4)) & 15u];
+        o[e] = lo | (hi << 16);
+    }
+    return (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+}
+
+// Bit pattern of one accumulator element (taken by value: a bit cast of a
+// vector element in place is not reliable).
+__device__ __forceinline__ uint32_t bits32(int x) { return (uint32_t)x; }
+__device__ __forceinline__ uint32_t bits32(float x) { return __float_as_uint(x); }
+
+__device__ __forceinline__ uint32_t dword_of(const uint4 &p, int i)
+{
+    return i == 0 ? p.x : i == 1 ? p.y : i == 2 ? p.z : p.w;
+}
 
 // Raw buffer resource (gfx9 layout): base address, stride 0, byte range,
 // default format word.  Offsets at or past `bytes` read as zero.
@@ -131,7 +169,7 @@ struct SplitK {
     int4 *part = nullptr;    // partial sums: [tile][part][8-byte piece][thread]
 };
 
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES>
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES, bool NF4 = false>
 struct TiledCfg {
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kWGN = WAVES / 2;              // wave grid: 2 along M, WAVES/2 along N
@@ -159,7 +197,12 @@ struct TiledCfg {
     static constexpr int kEpiRows = kWM < 64 ? kWM : 64;
     static constexpr int kEpiPitch = kWN * 2 + 16;
     static constexpr int kEpiBytes = F16OUT ? WAVES * kEpiRows * kEpiPitch : 0;
-    static constexpr int kLds = (STAGES * kStage > kEpiBytes) ? STAGES * kStage : kEpiBytes;
+    // NF4: each B row's 16 dequantized fp16 weights after the ring, rows
+    // 36 bytes apart (an odd number of dwords spreads the rows over the banks)
+    static constexpr int kTblPitch = 36;
+    static constexpr int kTblOff = STAGES * kStage;
+    static constexpr int kRing = STAGES * kStage + (NF4 ? BN * kTblPitch : 0);
+    static constexpr int kLds = (kRing > kEpiBytes) ? kRing : kEpiBytes;
     static_assert(kSA % 1024 == 0 && kSB % 1024 == 0, "whole 1 KB DMA blocks");
     static_assert(kLds <= 160 * 1024, "LDS");
     // 32 x 32 wave tiles read their operands a whole stage ahead instead of
@@ -173,7 +216,17 @@ struct TiledCfg {
 // FUSE: fp16 epilogue with the optional per-row activation scale (xscale,
 // NULL meaning 1) and the activation act; the plain fp16 epilogue has none.
 // SPLIT: the K split above (blockIdx.x = part * tiles + tile).
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE, bool SPLIT>
+// NF4: fp16 activations and 4-bit NF4 weight codes (BitBLAS custom-operator
+// guide, case 2).  A is fp16 [M, K/2] in the kernel's byte terms: K here is
+// the byte width of an A row (twice the number of k), so a stage of 128 A
+// bytes is 64 k, and the packed B row (K/4 bytes in these terms, two codes
+// per byte) has the int2 layout (BITS = 2).  `scale` is the per-row weight
+// scale and `xscale` the per-row zero point (NULL = 0): every workgroup
+// first builds its B rows' dequantized 16-entry tables in LDS,
+// fp16((table[c] - zero) * scale) in fp32; the matrix cores then take fp16
+// operands (v_mfma_f32_32x32x16_f16) and the fp32 sums go out as fp16.
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE, bool SPLIT,
+          bool NF4 = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, int act, void *__restrict__ C,
@@ -191,7 +244,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         }
     }
     using U = Unpack<BITS>;
-    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES>;
+    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES, NF4>;
+    static_assert(!NF4 || (BITS == 2 && F16OUT && !FUSE), "NF4: int2 byte layout, fp16 output, no fused epilogue");
     constexpr int kThreads = T::kThreads;
     static_assert(STAGES >= 2 && STAGES <= 8, "two to eight LDS stages");
     static_assert((STAGES - 2) * T::kDma < 64, "outstanding loads fit the wait counter");
@@ -331,12 +385,35 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         }
     };
 
-    v16i acc[T::kFM][T::kFN];
+    using Acc = typename std::conditional<NF4, v16f, v16i>::type;
+    Acc acc[T::kFM][T::kFN];
 #pragma unroll
     for (int i = 0; i < T::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < T::kFN; ++j)
-            acc[i][j] = (v16i){};
+            acc[i][j] = (Acc){};
+
+    // NF4: the dequantized table of each B row this lane feeds (one per
+    // fragment column j)
+    const uint16_t *tblRow[NF4 ? T::kFN : 1];
+    if constexpr (NF4) {
+        uint16_t *tbl = (uint16_t *)(lds + T::kTblOff);
+        for (int e = tid; e < BN * 16; e += kThreads) {
+            const int r = e >> 4, c = e & 15;
+            const int n = n0 + r;
+            float w = 0.0f;
+            if (n < N) {
+                const float sc1 = __half2float(__ushort_as_half(scale[n]));
+                const float z = xscale ? __half2float(__ushort_as_half(xscale[n])) : 0.0f;
+                const float d = __half2float(__ushort_as_half(kNf4TableF16[c])) - z;  // fp32, rounded
+                w = d * sc1;                                                          // fp32, rounded
+            }
+            tbl[r * (T::kTblPitch / 2) + c] = __half_as_ushort(__float2half_rn(w));
+        }
+#pragma unroll
+        for (int j = 0; j < T::kFN; ++j)
+            tblRow[j] = tbl + (wn * T::kWN + j * 32 + fr) * (T::kTblPitch / 2);
+    }
 
     // B operands of sub-step ks, unpacked from the packed 16-byte read that
     // feeds it (operand tt of that read)
@@ -346,7 +423,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
         for (int j = 0; j < T::kFN; ++j) {
             const uint4 &pk = fbp[pslot][j];
-            if constexpr (BITS == 8)
+            if constexpr (NF4)
+                bop[oslot][j] = decode_nf4(dword_of(pk, tt), tblRow[j]);
+            else if constexpr (BITS == 8)
                 bop[oslot][j] = U::template operand<0>(pk);
             else if constexpr (BITS == 4)
                 bop[oslot][j] = tt == 0 ? U::template operand<0>(pk) : U::template operand<1>(pk);
@@ -364,14 +443,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
             for (int i = i0; i < i1; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bop[oslot][j], fa[aslot][i], acc[i][j], 0, 0, 0);
+                acc[i][j] = mma32<NF4>(bop[oslot][j], fa[aslot][i], acc[i][j]);
     };
     constexpr int kHalf = T::kFM / 2;
     constexpr int kReads = T::kFM + T::kFN;
 
     // The lane's 4 x kFN groups of 4 consecutive scales for the fp16
     // epilogue, loaded before the K loop so their latency is hidden by it.
-    uint2 sc[F16OUT ? T::kFN : 1][4];
+    uint2 sc[(F16OUT && !NF4) ? T::kFN : 1][4];
     // with FUSE, the activation scale of each of the lane's kFM rows
     float xsv[FUSE ? T::kFM : 1];
     if constexpr (FUSE) {
@@ -381,7 +460,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             xsv[i] = !xscale ? 1.0f : m < M ? __half2float(__ushort_as_half(xscale[m])) : 0.0f;
         }
     }
-    if constexpr (F16OUT) {
+    if constexpr (F16OUT && !NF4) {
         const bool vecS = (N % 8) == 0;
 #pragma unroll
         for (int j = 0; j < T::kFN; ++j)
@@ -495,13 +574,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             for (int ks = 0; ks < 4; ++ks) {
                 v4i bo[T::kFN];
 #pragma unroll
-                for (int j = 0; j < T::kFN; ++j)
-                    bo[j] = U::operand_rt(gb[slot][ks / T::kSPR][j], ks % T::kSPR);
+                for (int j = 0; j < T::kFN; ++j) {
+                    if constexpr (NF4)
+                        bo[j] = decode_nf4(dword_of(gb[slot][0][j], ks), tblRow[j]);
+                    else
+                        bo[j] = U::operand_rt(gb[slot][ks / T::kSPR][j], ks % T::kSPR);
+                }
 #pragma unroll
                 for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
                     for (int i = 0; i < T::kFM; ++i)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bo[j], ga[slot][ks][i], acc[i][j], 0, 0, 0);
+                        acc[i][j] = mma32<NF4>(bo[j], ga[slot][ks][i], acc[i][j]);
             }
         };
         // One step: stage step+1 landed (the loads of STAGES-3 later stages
@@ -571,7 +654,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const uint64_t v = (uint32_t)acc[i][j][2 * q] | ((uint64_t)(uint32_t)acc[i][j][2 * q + 1] << 32);
+                    const uint64_t v = (uint64_t)bits32(acc[i][j][2 * q]) | ((uint64_t)bits32(acc[i][j][2 * q + 1]) << 32);
                     __hip_atomic_store(mine + ((i * T::kFN + j) * 8 + q) * kThreads, (long long)v,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -599,8 +682,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                     for (int q = 0; q < 8; ++q) {
                         const uint64_t v = (uint64_t)__hip_atomic_load(other + ((i * T::kFN + j) * 8 + q) * kThreads,
                                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        acc[i][j][2 * q] += (int)(uint32_t)v;
-                        acc[i][j][2 * q + 1] += (int)(uint32_t)(v >> 32);
+                        if constexpr (NF4) {
+                            acc[i][j][2 * q] += __uint_as_float((uint32_t)v);
+                            acc[i][j][2 * q + 1] += __uint_as_float((uint32_t)(v >> 32));
+                        } else {
+                            acc[i][j][2 * q] += (int)(uint32_t)v;
+                            acc[i][j][2 * q + 1] += (int)(uint32_t)(v >> 32);
+                        }
                     }
         }
     }
@@ -627,11 +715,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                     // scale / 2^kShift folds the exact int4/int2 rescaling into
                     // the multiply (a power-of-two factor, exact in fp32)
                     constexpr float kInv = 1.0f / (float)(1 << U::kShift);
-                    float s[4];
-                    s[0] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x & 0xFFFF))) * kInv;
-                    s[1] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x >> 16))) * kInv;
-                    s[2] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y & 0xFFFF))) * kInv;
-                    s[3] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y >> 16))) * kInv;
+                    float s[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // NF4: the scale is in the weights
+                    if constexpr (!NF4) {
+                        s[0] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x & 0xFFFF))) * kInv;
+                        s[1] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x >> 16))) * kInv;
+                        s[2] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y & 0xFFFF))) * kInv;
+                        s[3] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y >> 16))) * kInv;
+                    }
 #pragma unroll
                     for (int ii = 0; ii < kFragsPerPass; ++ii) {
                         const int i = i0 + ii;
@@ -641,7 +731,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                         float v[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? s[e] * xsv[i] : s[e]);
+                            if constexpr (NF4)
+                                v[e] = acc[i][j][4 * g + e];
+                            else
+                                v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? s[e] * xsv[i] : s[e]);
                             if constexpr (FUSE)
                                 v[e] = apply_act(v[e], act);
                         }
@@ -710,7 +803,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     }
 }
 
-template <int BITS, int BM, int BN, int STAGES, int WAVES, bool SPLIT = false>
+template <int BITS, int BM, int BN, int STAGES, int WAVES, bool SPLIT = false, bool NF4 = false>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
                     int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
                     const SplitK &sk = {})
@@ -718,10 +811,13 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
     const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
     const dim3 grid((unsigned)(tilesM * tilesN * (SPLIT ? sk.parts : 1)), (unsigned)batch);
     const bool tail = (K % kBK) != 0;
-#define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                              \
-    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED, SPLIT><<<grid, 64 * WAVES, 0, s>>>( \
+#define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                                   \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED, SPLIT, NF4><<<grid, 64 * WAVES, 0, s>>>( \
         A, B, scale, xscale, act, C, M, N, K, tilesM, tilesN, bs, sk)
-    if (scale && (xscale || act != 0)) {
+    if constexpr (NF4) {
+        // the row width of A is a whole number of 128-byte stages (K % 64 == 0)
+        BQ_TILED_LAUNCH(true, false, false);
+    } else if (scale && (xscale || act != 0)) {
         if (tail)
             BQ_TILED_LAUNCH(true, true, true);
         else
@@ -809,7 +905,7 @@ bool split_workspace(hipStream_t s, SplitK &sk)
     return true;
 }
 
-template <int BITS>
+template <int BITS, bool NF4 = false>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
                        int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
@@ -819,11 +915,11 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
-        return launch_t<BITS, 256, 256, kStages256, 8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 256, 256, kStages256, 8, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 128, 128, 3, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (t64 >= 512)
-        return launch_t<BITS, 64, 64, 4, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 64, 64, 4, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (batch == 1 && t64 <= kSplitMaxTiles) {
         const int stepsAll = (K + kBK - 1) / kBK;
         int parts = min(kSplitMaxParts, min(kSplitMaxWgs / (int)t64, stepsAll / kSplitMinSteps));
@@ -832,13 +928,22 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
             // equal stage counts; the rounding never leaves a workgroup empty
             sk.stepsPer = (stepsAll + parts - 1) / parts;
             sk.parts = (stepsAll + sk.stepsPer - 1) / sk.stepsPer;
-            return launch_t<BITS, 64, 64, 8, 4, true>(A, B, scale, xscale, act, C, M, N, K, 1, bs, s, sk);
+            return launch_t<BITS, 64, 64, 8, 4, true, NF4>(A, B, scale, xscale, act, C, M, N, K, 1, bs, s, sk);
         }
     }
-    return launch_t<BITS, 64, 64, 8, 4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 64, 64, 8, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
 }
 
 }  // namespace
+
+hipError_t launch_gemm_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero,
+                           uint16_t *C, int M, int N, int K, hipStream_t s)
+{
+    if (M == 0 || N == 0)
+        return hipSuccess;
+    // in the kernel's byte terms an A row is 2K bytes wide (see the kernel)
+    return launch_bits<2, true>((const int8_t *)A, B, scale, zero, 0, C, M, N, 2 * K, 1, {}, s);
+}
 
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
                              const uint16_t *scale, const uint16_t *xscale, int act, void *C,

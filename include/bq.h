@@ -270,6 +270,33 @@ int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f1
                 const void *x_scale_f16, int act, void *C_f16, int64_t M, int64_t N, int64_t K,
                 int path, void *stream);
 
+/*
+ * bq_gemm_nf4_a16 - W4A16 GEMM with NF4 weight codes, fp16 activations and
+ * fp32 accumulation (BitBLAS guide, case 2: A fp16 [M, K], B_nf4 uint8
+ * [N, K/2], scale and zero_point fp16 [N], C = sum_k fp32(A) * fp32(W)).
+ * The page leaves out the NF4 table and the dequantization; readings:
+ *   table[16]  the 4-bit NormalFloat codebook (QLoRA: normal quantiles,
+ *              eight positive, seven negative, and zero, scaled to [-1, 1]),
+ *              held in fp16; code c selects the c-th smallest value
+ *   W[n,k]     fp16(fp32(fp32(table[c] - zero[n]) * scale[n])), one fp16
+ *              rounding (nearest even); zero NULL means 0
+ *   C[m,n]     fp16 of sum_k A[m,k] * W[n,k] accumulated in fp32 by the
+ *              matrix cores; within one fp16 ulp of the exact sum's value
+ *              plus the fp32 accumulation bound K 2^-24 sum_k |A W|
+ *
+ *   A_f16      [M, K] fp16 row-major
+ *   B          [N, K/2] uint8: code of k even in the low nibble, k odd in
+ *              the high nibble (codes 0..15)
+ *   scale_f16  [N] fp16 (required); zero_f16 [N] fp16 or NULL
+ *   C_f16      [M, N] fp16
+ * M, N >= 0; 0 <= K <= BQ_MAX_K, K % 64 == 0 (BQ_ERR_SHAPE); pointers
+ * 16-byte aligned (BQ_ERR_ALIGN); NULL where required (BQ_ERR_NULL).  Runs
+ * on the tiled matrix-core kernel for every M (with the K split of the
+ * conventions above when the output has few 64 x 64 tiles).
+ */
+int bq_gemm_nf4_a16(const void *A_f16, const uint8_t *B, const void *scale_f16, const void *zero_f16,
+                    void *C_f16, int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Which kernel path BQ_PATH_AUTO takes for this shape (BQ_PATH_GEMV,
  * BQ_PATH_STREAM or BQ_PATH_TILED).  Host-only integer logic; no device call. */
 int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits);

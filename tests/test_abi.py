@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -147,3 +147,18 @@ def test_quantize_and_pack_validation(bq):
     assert L.bq_pack_int2(P16, 4, 8, PODD, S) == bq.BQ_ERR_ALIGN
     assert L.bq_pack_int4(NULL, 0, 8, NULL, S) == bq.BQ_OK
     assert L.bq_pack_int2(NULL, 4, 0, NULL, S) == bq.BQ_OK
+
+
+def test_nf4_validation(bq):
+    L = bq.lib()
+    S = NULL
+    f = L.bq_gemm_nf4_a16
+    assert f(P16, P16b, P16c, NULL, P16d, 4, 4, 96, S) == bq.BQ_ERR_SHAPE   # K % 64
+    assert f(P16, P16b, P16c, NULL, P16d, -1, 4, 64, S) == bq.BQ_ERR_SHAPE
+    assert f(P16, P16b, P16c, NULL, P16d, 4, 4, 65536 + 64, S) == bq.BQ_ERR_SHAPE
+    assert f(P16, P16b, NULL, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_NULL    # scale required
+    assert f(NULL, P16b, P16c, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_NULL
+    assert f(P16, P16b, P16c, PODD, P16d, 4, 4, 64, S) == bq.BQ_ERR_ALIGN   # zero point
+    assert f(P16, PODD, P16c, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_ALIGN
+    assert f(NULL, NULL, NULL, NULL, NULL, 0, 4, 64, S) == bq.BQ_OK
+    assert f(NULL, NULL, NULL, NULL, NULL, 4, 0, 64, S) == bq.BQ_OK

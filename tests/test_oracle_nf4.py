@@ -245,3 +245,17 @@ def test_tolerance_covers_sequential_fp32_sum():
             assert d <= 1  # same sign here; in practice one ulp at most
             off_by_one += d
     assert off_by_one <= M * N // 10
+
+
+def test_library_table_matches_the_oracle():
+    """The fp16 table compiled into the HIP library (written by its own
+    generator, Newton's method on math.erf) equals the oracle's."""
+    import os
+    import re
+
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "bit_mixed_precision_amd", "csrc", "nf4_table.h")
+    text = open(path).read()
+    body = text[text.index("kNf4TableF16"):]
+    vals = [int(h, 16) for h in re.findall(r"0x([0-9A-Fa-f]{4})", body)]
+    assert vals == nf4.nf4_table_f16().tolist()
