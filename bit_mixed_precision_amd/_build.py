@@ -10,7 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(_HERE, "csrc")
 OBJDIR = os.path.join(_HERE, "_build")
 LIB = os.path.join(_HERE, "libbq.so")
-SOURCES = ["api.hip", "quantize.hip", "pack.hip", "gemv.hip", "gemm_stream.hip", "gemm_tiled.hip"]
+SOURCES = ["api.hip", "quantize.hip", "pack.hip", "gemv.hip", "gemv_nf4.hip", "gemm_stream.hip", "gemm_tiled.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -281,6 +281,10 @@ int bq_gemm_nf4_a16(const void *A_f16, const uint8_t *B, const void *scale_f16, 
     const int st = check_device();
     if (st != BQ_OK)
         return st;
+    if (M <= kGemvMaxM)
+        return launch_status(bq::launch_gemv_nf4((const uint16_t *)A_f16, B, (const uint16_t *)scale_f16,
+                                                 (const uint16_t *)zero_f16, (uint16_t *)C_f16, (int)M, (int)N,
+                                                 (int)K, (hipStream_t)stream));
     return launch_status(bq::launch_gemm_nf4((const uint16_t *)A_f16, B, (const uint16_t *)scale_f16,
                                              (const uint16_t *)zero_f16, (uint16_t *)C_f16, (int)M, (int)N,
                                              (int)K, (hipStream_t)stream));

@@ -67,5 +67,8 @@ hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
 // codes [N, K/2], per-row scale and zero point (zero may be NULL), C fp16.
 hipError_t launch_gemm_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero,
                            uint16_t *C, int M, int N, int K, hipStream_t s);
+// The same product for M <= 4 as a stream over B (decode).
+hipError_t launch_gemv_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero,
+                           uint16_t *C, int M, int N, int K, hipStream_t s);
 
 }  // namespace bq

@@ -405,8 +405,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             if (n < N) {
                 const float sc1 = __half2float(__ushort_as_half(scale[n]));
                 const float z = xscale ? __half2float(__ushort_as_half(xscale[n])) : 0.0f;
-                const float d = __half2float(__ushort_as_half(kNf4TableF16[c])) - z;  // fp32, rounded
-                w = d * sc1;                                                          // fp32, rounded
+                // two fp32 roundings, then one to fp16; the empty asm keeps the
+                // multiply from being fused with the conversion (one rounding)
+                const float d = __half2float(__ushort_as_half(kNf4TableF16[c])) - z;
+                w = d * sc1;
+                asm volatile("" : "+v"(w));
             }
             tbl[r * (T::kTblPitch / 2) + c] = __half_as_ushort(__float2half_rn(w));
         }

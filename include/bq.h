@@ -290,8 +290,9 @@ int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f1
  *   scale_f16  [N] fp16 (required); zero_f16 [N] fp16 or NULL
  *   C_f16      [M, N] fp16
  * M, N >= 0; 0 <= K <= BQ_MAX_K, K % 64 == 0 (BQ_ERR_SHAPE); pointers
- * 16-byte aligned (BQ_ERR_ALIGN); NULL where required (BQ_ERR_NULL).  Runs
- * on the tiled matrix-core kernel for every M (with the K split of the
+ * 16-byte aligned (BQ_ERR_ALIGN); NULL where required (BQ_ERR_NULL).  M <= 4
+ * runs a decode GEMV (dot products on the vector ALUs, a stream over B);
+ * larger M the tiled matrix-core kernel (with the K split of the
  * conventions above when the output has few 64 x 64 tiles).
  */
 int bq_gemm_nf4_a16(const void *A_f16, const uint8_t *B, const void *scale_f16, const void *zero_f16,

@@ -105,3 +105,32 @@ def test_nf4_k_zero_gives_zeros(dev):
     C = bq.gemm_nf4_a16(A, B, s, out=torch.full((5, 7), 3.0, dtype=torch.float16, device=dev))
     torch.cuda.synchronize()
     assert torch.count_nonzero(C).item() == 0
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_nf4_dequantized_weights_bit_exact(dev, M):
+    """One-hot activation rows (A[m, k_m] = 1) make C[m, n] = W[n, k_m]
+    exactly, so the GPU's dequantized weights -- fp16(fp32(table[c] - zero)
+    * scale), two fp32 roundings then one to fp16 -- are compared bit for bit
+    with the oracle's, for scales and zero points over a wide range
+    (subnormal to 2^10), on the decode GEMV (M = 4) and the tiled kernel
+    (up to the sign of zero: an exact sum of +0 and -0 terms is +0)."""
+    N, K = 300, 256
+    banner(f"nf4 dequantized weights M={M}")
+    g = np.random.default_rng(M)
+    codes = g.integers(0, 16, (N, K)).astype(np.uint8)
+    s = (g.choice([1, -1], N) * 2.0 ** g.integers(-24, 11, N) * (1 + g.integers(0, 1024, N) / 1024))
+    z = (g.choice([1, -1], N) * 2.0 ** g.integers(-24, 4, N) * (1 + g.integers(0, 1024, N) / 1024))
+    s = s.astype(np.float16).view(np.uint16)
+    z = z.astype(np.float16).view(np.uint16)
+    ks = g.choice(K, M, replace=False)
+    A = np.zeros((M, K), np.float16)
+    A[np.arange(M), ks] = 1.0
+    Bp = nf4.pack_codes(codes)
+    C = _run(dev, A.view(np.uint16), Bp, s, z)
+    W = nf4.dequant_nf4(Bp, K, s, z)
+    # a sum whose only nonzero term is -0 is +0
+    want = np.where(W[:, ks].T == 0x8000, 0, W[:, ks].T).astype(np.uint16)
+    bad = np.argwhere(C != want)
+    assert len(bad) == 0, (f"{len(bad)} of {C.size} weights differ; first: " +
+                           ", ".join(f"got {C[i, j]:#06x} want {want[i, j]:#06x}" for i, j in bad[:8]))
