@@ -332,7 +332,45 @@ def main():
     prep_p_us = float(np.mean([e[1].elapsed_time(e[2]) for e in prep_ev])) * 1e3
     prep_bytes = roofline.quantize_bytes(*W.shape) + roofline.pack_bytes(W.shape[0], W.shape[1], 4)
 
+    # W4A16 with NF4 weight codes, per-row scale and zero point: decode
+    # (M = 1, a stream over the codes, bound by HBM) and prefill (M = 4096,
+    # fp16 matrix cores), N = K = 4096, code rings past the MALL.
+    nf4_res = {}
+    g16 = np.random.default_rng(7)
+    s_nf = up(g16.uniform(0.001, 0.01, 4096).astype(np.float16))
+    z_nf = up(g16.uniform(-0.05, 0.05, 4096).astype(np.float16))
+    codes_nf = torch.from_numpy(g16.integers(0, 256, (4096, K // 2), dtype=np.uint8)).to(dev)
+    nf_ring = ring(codes_nf, ring_len(codes_nf.numel()))
+    for Mn in (1, 4096):
+        A_nf = up(g16.standard_normal((Mn, K)).astype(np.float16))
+        C_nf = torch.empty((Mn, 4096), dtype=torch.float16, device=dev)
+        nf_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.warmup):
+            bq.gemm_nf4_a16(A_nf, nf_ring[i % len(nf_ring)], s_nf, z_nf, out=C_nf)
+        torch.cuda.synchronize()
+        hold_gpu()
+        for i in range(args.steps):
+            nf_ev[i][0].record()
+            bq.gemm_nf4_a16(A_nf, nf_ring[i % len(nf_ring)], s_nf, z_nf, out=C_nf)
+            nf_ev[i][1].record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e[0].elapsed_time(e[1]) for e in nf_ev])) * 1e3
+        nbytes = roofline.nf4_gemm_bytes(Mn, 4096, K)
+        flops = roofline.gemm_ops(Mn, 4096, K)
+        key = "w4a16_nf4_m%d" % Mn
+        if Mn == 1:
+            nf4_res[key] = {"shape": [Mn, 4096, K], "kernel": "gemv_nf4_kernel", "us": round(us, 2),
+                            "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / roofline.HBM_PEAK_BYTES_PER_S, 4)}
+        else:
+            nf4_res[key] = {"shape": [Mn, 4096, K], "kernel": "gemm_tiled_kernel (NF4 mode)", "us": round(us, 2),
+                            "TFLOP_per_s": round(flops / (us * 1e-6) / 1e12, 1),
+                            "frac_of_fp16_mfma_peak": round(flops / (us * 1e-6) / roofline.FP16_MFMA_PEAK_FLOPS, 4)}
+        del A_nf, C_nf
+    del nf_ring, codes_nf
+
     extras = {
+        **nf4_res,
         "weight_prep_int4": {
             "shape": list(W.shape), "quantize_us": round(prep_q_us, 2), "pack_us": round(prep_p_us, 2),
             "GB_per_s": round(prep_bytes / ((prep_q_us + prep_p_us) * 1e-6) / 1e9, 1),

@@ -14,6 +14,7 @@ from __future__ import annotations
 # MI355X published peaks (dense, no sparsity).
 HBM_PEAK_BYTES_PER_S = 8.0e12
 INT8_MFMA_PEAK_OPS_PER_S = 5.0e15
+FP16_MFMA_PEAK_FLOPS = 2.5e15
 FP32_VECTOR_PEAK_FLOPS = 157.3e12
 
 
@@ -40,6 +41,12 @@ def gemm_bytes(M: int, N: int, K: int, bits: int, out: str = "f16") -> int:
     else:
         b += 4 * M * N
     return b
+
+
+def nf4_gemm_bytes(M: int, N: int, K: int, zero: bool = True) -> int:
+    """W4A16: fp16 A [M,K] + 4-bit codes [N,K] + fp16 scale (and zero point)
+    [N] + fp16 output [M,N]."""
+    return 2 * M * K + (N * K) // 2 + (4 if zero else 2) * N + 2 * M * N
 
 
 def quantize_bytes(rows: int, cols: int) -> int:
