@@ -36,6 +36,10 @@
 //    stage ahead.
 //  * Epilogue: fp16(acc * scale) rows are staged through LDS and written
 //    with 16-byte coalesced stores.
+//  * With few output tiles, K is split over several workgroups per tile;
+//    the last to finish adds the others' partial sums (SplitK below).
+//  * An NF4 mode (fp16 activations, 4-bit NormalFloat weight codes) reuses
+//    the same ring and loops with fp16 matrix-core operands (see the kernel).
 // Workgroups are mapped so that the tiles one XCD runs (blockIdx modulo 8
 // picks the XCD) form a compact block of the output, sharing A and B rows in
 // that XCD's L2.
