@@ -848,8 +848,10 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
 // hundred workgroups.  Measured on MI355X at N = K = 4096 (W4A8):
 //  * 256 x 256, eight wavefronts (2 x 4 of 128 x 64), once there are 256
 //    such tiles (M >= 4096);
-//  * 128 x 128, four wavefronts (64 x 64 each), from 192 tiles (M >= 768:
-//    25 us at M = 1024, 43 us at M = 2048 where the 256 x 256 tiles take 49);
+//  * 128 x 128 from 192 tiles (M >= 768), eight wavefronts (64 x 32 each)
+//    for int4 / int2, four (64 x 64) for int8: W4A8 22 us at M = 768 and
+//    25 us at M = 1024 (24 / 27.6 with four wavefronts), 43 us at M = 2048
+//    where the 256 x 256 tiles take 49;
 //  * 64 x 64, four wavefronts (32 x 32 each), a 4-stage ring, from 512 tiles
 //    (several workgroups per CU; 17 us at M = 512, against 22 us with
 //    128 x 128 tiles);
@@ -923,8 +925,11 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
         return launch_t<BITS, 256, 256, kStages256, 8, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    // 128 x 128: eight wavefronts (2 x 4 of 64 x 32) for the packed widths,
+    // four (64 x 64 each) for int8
+    constexpr int kWaves128 = BITS == 8 ? 4 : 8;
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 128, 128, 3, kWaves128, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (t64 >= 512)
         return launch_t<BITS, 64, 64, 4, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     if (batch == 1 && t64 <= kSplitMaxTiles) {
