@@ -66,8 +66,9 @@ def _random_case(M, N, K, seed, zero=True):
     return A, nf4.pack_codes(codes), s, z
 
 
-RANDOM_SHAPES = [(1, 4096, 4096), (1, 11008, 4096), (16, 256, 256), (64, 4096, 4096),
-                 (300, 260, 1024), (300, 2000, 4096), (1030, 1100, 512), (4096, 4096, 512)]
+RANDOM_SHAPES = [(1, 4096, 4096), (1, 11008, 4096), (2, 301, 512), (3, 777, 64), (4, 130, 65536),
+                 (5, 64, 128), (16, 256, 256), (64, 4096, 4096), (300, 260, 1024), (300, 2000, 4096),
+                 (1030, 1100, 512), (4096, 4096, 512)]
 
 
 @pytest.mark.parametrize("shape", RANDOM_SHAPES)
