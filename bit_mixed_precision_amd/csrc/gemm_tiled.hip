@@ -173,10 +173,12 @@ struct SplitK {
     int4 *part = nullptr;    // partial sums: [tile][part][8-byte piece][thread]
 };
 
-template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES, bool NF4 = false>
+// WGM: wavefronts along M (2, or 1 for a 1 x WAVES grid whose wave tiles
+// span all BM rows, so that each B column is decoded by one wavefront).
+template <int BITS, int BM, int BN, int STAGES, bool F16OUT, int WAVES, bool NF4 = false, int WGM = 2>
 struct TiledCfg {
     static constexpr int kThreads = 64 * WAVES;
-    static constexpr int kWGN = WAVES / 2;              // wave grid: 2 along M, WAVES/2 along N
+    static constexpr int kWGN = WAVES / WGM;            // wave grid: WGM along M, WAVES/WGM along N
     static constexpr int kPB = kBK * BITS / 8;          // packed B bytes per row per stage
     static constexpr int kCPR = kPB / 16;               // B 16-byte chunks per row
     static constexpr int kRowsPerLineB = 256 / kPB;     // B rows sharing a 256-byte bank line
@@ -193,7 +195,7 @@ struct TiledCfg {
     static constexpr int kDmaB = (kBlkB + WAVES - 1) / WAVES;
     static constexpr bool kEvenA = kBlkA % WAVES == 0, kEvenB = kBlkB % WAVES == 0;
     static constexpr int kDma = kDmaA + kDmaB;          // DMA instructions per stage, upper bound per wave
-    static constexpr int kWM = BM / 2, kWN = BN / kWGN; // wave tile
+    static constexpr int kWM = BM / WGM, kWN = BN / kWGN; // wave tile
     static constexpr int kFM = kWM / 32;                // 32x32 fragments per wave along M
     static constexpr int kFN = kWN / 32;                // and N
     static constexpr int kSPR = 8 / BITS;               // sub-steps fed by one packed 16-byte read
@@ -230,7 +232,7 @@ struct TiledCfg {
 // fp16((table[c] - zero) * scale) in fp32; the matrix cores then take fp16
 // operands (v_mfma_f32_32x32x16_f16) and the fp32 sums go out as fp16.
 template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE, bool SPLIT,
-          bool NF4 = false>
+          bool NF4 = false, int WGM = 2>
 __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     const int8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ xscale, int act, void *__restrict__ C,
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         }
     }
     using U = Unpack<BITS>;
-    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES, NF4>;
+    using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES, NF4, WGM>;
     static_assert(!NF4 || (BITS == 2 && F16OUT && !FUSE), "NF4: int2 byte layout, fp16 output, no fused epilogue");
     constexpr int kThreads = T::kThreads;
     static_assert(STAGES >= 2 && STAGES <= 8, "two to eight LDS stages");
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     }
 }
 
-template <int BITS, int BM, int BN, int STAGES, int WAVES, bool SPLIT = false, bool NF4 = false>
+template <int BITS, int BM, int BN, int STAGES, int WAVES, bool SPLIT = false, bool NF4 = false, int WGM = 2>
 hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
                     int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
                     const SplitK &sk = {})
@@ -819,7 +821,7 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
     const dim3 grid((unsigned)(tilesM * tilesN * (SPLIT ? sk.parts : 1)), (unsigned)batch);
     const bool tail = (K % kBK) != 0;
 #define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                                   \
-    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED, SPLIT, NF4><<<grid, 64 * WAVES, 0, s>>>( \
+    gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED, SPLIT, NF4, WGM><<<grid, 64 * WAVES, 0, s>>>( \
         A, B, scale, xscale, act, C, M, N, K, tilesM, tilesN, bs, sk)
     if constexpr (NF4) {
         // the row width of A is a whole number of 128-byte stages (K % 64 == 0)
@@ -924,14 +926,22 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
-        return launch_t<BITS, 256, 256, kStages256, 8, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        // NF4: a 1 x 8 wavefront grid (256 x 32 each), so each B column's
+        // codes are looked up by one wavefront instead of two
+        return launch_t<BITS, 256, 256, kStages256, 8, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
+                                                                               batch, bs, s);
     // 128 x 128: eight wavefronts (2 x 4 of 64 x 32) for the packed widths,
-    // four (64 x 64 each) for int8
-    constexpr int kWaves128 = BITS == 8 ? 4 : 8;
+    // four (64 x 64 each) for int8; NF4: four in a 1 x 4 grid (128 x 32
+    // each), so each B column's codes are looked up by one wavefront
+    constexpr int kWaves128 = NF4 ? 4 : BITS == 8 ? 4 : 8;
+    // 64 x 64: four wavefronts (2 x 2 of 32 x 32); NF4 two (1 x 2 of 64 x 32)
+    constexpr int kWaves64 = NF4 ? 2 : 4;
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, kWaves128, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 128, 128, 3, kWaves128, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
+                                                                              batch, bs, s);
     if (t64 >= 512)
-        return launch_t<BITS, 64, 64, 4, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+        return launch_t<BITS, 64, 64, 4, kWaves64, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
+                                                                           batch, bs, s);
     if (batch == 1 && t64 <= kSplitMaxTiles) {
         const int stepsAll = (K + kBK - 1) / kBK;
         int parts = min(kSplitMaxParts, min(kSplitMaxWgs / (int)t64, stepsAll / kSplitMinSteps));
@@ -940,10 +950,12 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
             // equal stage counts; the rounding never leaves a workgroup empty
             sk.stepsPer = (stepsAll + parts - 1) / parts;
             sk.parts = (stepsAll + sk.stepsPer - 1) / sk.stepsPer;
-            return launch_t<BITS, 64, 64, 8, 4, true, NF4>(A, B, scale, xscale, act, C, M, N, K, 1, bs, s, sk);
+            return launch_t<BITS, 64, 64, 8, kWaves64, true, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K, 1,
+                                                                              bs, s, sk);
         }
     }
-    return launch_t<BITS, 64, 64, 8, 4, false, NF4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    return launch_t<BITS, 64, 64, 8, kWaves64, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K, batch,
+                                                                         bs, s);
 }
 
 }  // namespace
