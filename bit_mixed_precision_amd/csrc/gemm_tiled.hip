@@ -851,9 +851,10 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
 //  * 256 x 256, eight wavefronts (2 x 4 of 128 x 64), once there are 256
 //    such tiles (M >= 4096);
 //  * 128 x 128 from 192 tiles (M >= 768), eight wavefronts (64 x 32 each)
-//    for int4 / int2, four (64 x 64) for int8: W4A8 22 us at M = 768 and
-//    25 us at M = 1024 (24 / 27.6 with four wavefronts), 43 us at M = 2048
-//    where the 256 x 256 tiles take 49;
+//    for int4, four for int8 (64 x 64) and int2 (128 x 32): W4A8 22 us at
+//    M = 768 and 25 us at M = 1024 (24 / 27.6 with four wavefronts), 43 us at
+//    M = 2048 where the 256 x 256 tiles take 49; W2A8 24.4 us at M = 1024
+//    (27.8 with eight 64 x 32 wave tiles);
 //  * 64 x 64, four wavefronts (32 x 32 each), a 4-stage ring, from 512 tiles
 //    (several workgroups per CU; 17 us at M = 512, against 22 us with
 //    128 x 128 tiles);
@@ -930,15 +931,16 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
         // codes are looked up by one wavefront instead of two
         return launch_t<BITS, 256, 256, kStages256, 8, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
                                                                                batch, bs, s);
-    // 128 x 128: eight wavefronts (2 x 4 of 64 x 32) for the packed widths,
-    // four (64 x 64 each) for int8; NF4: four in a 1 x 4 grid (128 x 32
-    // each), so each B column's codes are looked up by one wavefront
-    constexpr int kWaves128 = NF4 ? 4 : BITS == 8 ? 4 : 8;
+    // 128 x 128: int4 eight wavefronts (2 x 4 of 64 x 32); int8 four (2 x 2
+    // of 64 x 64); int2 and NF4 four in a 1 x 4 grid (128 x 32 each), so each
+    // B column is unpacked or looked up by one wavefront
+    constexpr int kWaves128 = BITS == 4 ? 8 : 4;
+    constexpr int kWgm128 = BITS == 2 ? 1 : 2;
     // 64 x 64: four wavefronts (2 x 2 of 32 x 32); NF4 two (1 x 2 of 64 x 32)
     constexpr int kWaves64 = NF4 ? 2 : 4;
     if (t128 >= 192)
-        return launch_t<BITS, 128, 128, 3, kWaves128, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
-                                                                              batch, bs, s);
+        return launch_t<BITS, 128, 128, 3, kWaves128, false, NF4, kWgm128>(A, B, scale, xscale, act, C, M, N, K, batch,
+                                                                          bs, s);
     if (t64 >= 512)
         return launch_t<BITS, 64, 64, 4, kWaves64, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
                                                                            batch, bs, s);
