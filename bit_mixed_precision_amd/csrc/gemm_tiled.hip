@@ -8,8 +8,9 @@
 //
 // Decomposition (Pallas page, blocked matmul: output blocks independent, the
 // K blocks accumulated in sequence): a workgroup owns a BM x BN output tile
-// (256 x 256 with eight wavefronts, 128 x 128 or 64 x 64 with four; chosen by
-// the number of tiles, see launch_bits) and walks K in stages of 128.
+// (256 x 256, 128 x 128 or 64 x 64, with two to eight wavefronts; chosen by
+// the number of tiles and the width of B, see launch_bits) and walks K in
+// stages of 128.
 //
 //  * Global -> LDS without registers: 16-byte buffer loads with the LDS-DMA
 //    form (lane i of a load writes LDS bytes [M0 + 16 i, +16)).  Rows past
@@ -23,8 +24,9 @@
 //    bank groups (rows of 128 / 64 / 32 bytes use the row bits above the
 //    2 / 4 / 8 rows that share one 256-byte bank line).  The load lanes are
 //    permuted so that the DMA writes exactly this layout.
-//  * Wavefronts form a 2 x (WAVES/2) grid over the tile and compute with
-//    v_mfma_i32_32x32x32_i8, B fragments as the instruction's first operand
+//  * Wavefronts form a 2 x (WAVES/2) grid over the tile (1 x WAVES for
+//    some configurations, so that one wavefront unpacks each B column) and
+//    compute with v_mfma_i32_32x32x32_i8, B fragments as the first operand
 //    (so the accumulator holds C transposed: each lane owns 4 consecutive n
 //    of one row m), A fragments as the second.  Per 32-k sub-step a lane
 //    feeds 16 consecutive k of each operand; packed B is read 16 bytes at a
@@ -66,7 +68,6 @@ constexpr uint32_t kOOB = 0x80000000u;  // buffer offset that is always out of r
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
