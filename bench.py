@@ -54,9 +54,18 @@ def parse():
 
 
 # Kernel sources of the tiled matrix-core GEMM; the committed HBM-traffic
-# summary is used only while these files and the compiler flags are unchanged.
-TILED_SOURCES = ["gemm_tiled.hip", "unpack.h", "bq_internal.h"]
+# summary is used only while their code (comments and blank space aside) and
+# the compiler flags are unchanged.
+TILED_SOURCES = ["gemm_tiled.hip", "unpack.h", "bq_internal.h", "nf4_table.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a8_m4096_hbm_traffic.txt")
+
+
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace (string literals kept)."""
+    import re
+
+    token = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\s+', re.S)
+    return token.sub(lambda m: m.group(0) if m.group(0).startswith('"') else "", text)
 
 
 def tiled_source_hash() -> str:
@@ -66,8 +75,8 @@ def tiled_source_hash() -> str:
 
     h = hashlib.sha256()
     for f in TILED_SOURCES:
-        with open(os.path.join(ROOT, "bit_mixed_precision_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_mixed_precision_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     h.update(" ".join(_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
