@@ -552,11 +552,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     } else {
         // ---- stage-ahead loop (32 x 32 wave tiles): a wave's operands for a
         // whole stage are read right after the barrier that publishes the
-        // stage, one stage before they are used.
+        // stage, one step before they are used.  With a ring of six stages or
+        // more a step covers two stages (SPS), so one barrier serves two.
         constexpr int kPk = 4 / T::kSPR;  // packed B reads per stage
-        v4i ga[2][4][T::kFM];
-        uint4 gb[2][kPk][T::kFN];
-        auto read_stage = [&](int step, int slot) {
+        constexpr int SPS = STAGES >= 6 ? 2 : 1;
+        v4i ga[2][SPS][4][T::kFM];
+        uint4 gb[2][SPS][kPk][T::kFN];
+        auto read_stage = [&](int step, int slot, int u) {
             const int8_t *la = lds + (step % STAGES) * T::kStage;
             const int8_t *lb = la + T::kSA;
 #pragma unroll
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                 for (int i = 0; i < T::kFM; ++i) {
                     const int row = wm * T::kWM + i * 32 + fr;
-                    ga[slot][ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+                    ga[slot][u][ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
                 }
             }
 #pragma unroll
@@ -574,70 +576,90 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                 for (int j = 0; j < T::kFN; ++j) {
                     const int row = wn * T::kWN + j * 32 + fr;
-                    gb[slot][q][j] = *(const uint4 *)(lb + row * T::kPB +
-                                                      ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+                    gb[slot][u][q][j] = *(const uint4 *)(lb + row * T::kPB +
+                                                         ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
                 }
             }
         };
-        auto compute_stage = [&](int slot) {
+        auto compute_stage = [&](int slot, int u) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 v4i bo[T::kFN];
 #pragma unroll
                 for (int j = 0; j < T::kFN; ++j) {
                     if constexpr (NF4)
-                        bo[j] = decode_nf4(dword_of(gb[slot][0][j], ks), tblRow[j]);
+                        bo[j] = decode_nf4(dword_of(gb[slot][u][0][j], ks), tblRow[j]);
                     else
-                        bo[j] = U::operand_rt(gb[slot][ks / T::kSPR][j], ks % T::kSPR);
+                        bo[j] = U::operand_rt(gb[slot][u][ks / T::kSPR][j], ks % T::kSPR);
                 }
 #pragma unroll
                 for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
                     for (int i = 0; i < T::kFM; ++i)
-                        acc[i][j] = mma32<NF4>(bo[j], ga[slot][ks][i], acc[i][j]);
+                        acc[i][j] = mma32<NF4>(bo[j], ga[slot][u][ks][i], acc[i][j]);
             }
         };
-        // One step: stage step+1 landed (the loads of STAGES-3 later stages
-        // may still be in flight) and this wave's reads of two steps ago done,
-        // then the barrier; after it, the loads of stage step+STAGES-1 go into
-        // the slot those reads used, the operands of stage step+1 are read
-        // and stage step is computed from the operands read one step ago.
-        // Only the reads of two steps ago are waited for at the barrier, so
-        // the latest reads stay in flight across it.  The scheduling fences
-        // keep the unpack of the operands just read (register work) from being
-        // hoisted next to the reads.  Unrolled by two so the operand slots are
-        // compile-time register indices.
-        constexpr int kReadsStep = 4 * T::kFM + kPk * T::kFN;
-        auto one_step = [&](int step, int cur) {
+        // One step (stages step .. step+SPS-1): stages step+SPS ..
+        // step+2SPS-1 landed (of the stages issued so far, through
+        // step+STAGES-SPS-1, the last STAGES-3SPS may still be in flight) and
+        // this wave's reads of two steps ago done, then the barrier; after it,
+        // the loads of stages step+STAGES-SPS .. step+STAGES-1 go into the
+        // slots those reads used, the operands of the next step's stages are
+        // read and this step's stages are computed from the operands read one
+        // step ago.  Only the reads of two steps ago are waited for at the
+        // barrier (all but the last 15 when a step reads more), so the latest
+        // reads stay in flight across it.  The scheduling fences keep the
+        // unpack of the operands just read (register work) from being hoisted
+        // next to the reads.  Steps are unrolled by two so the operand slots
+        // are compile-time register indices; in the last steps, stages past
+        // the end are read (in range, never used) but not computed.
+        constexpr int kReadsStage = 4 * T::kFM + kPk * T::kFN;
+        constexpr int kReadsStep = SPS * kReadsStage < 15 ? SPS * kReadsStage : 15;
+        auto one_step = [&](int step, int cur, bool full) {
             if constexpr (T::kEvenA && T::kEvenB)
-                wait_vmcnt<(STAGES - 3) * T::kDma>();
+                wait_vmcnt<(STAGES - 3 * SPS) * T::kDma>();
             else
-                wait_vmcnt_rt<STAGES - 3, T::kDma>(myDma);
+                wait_vmcnt_rt<STAGES - 3 * SPS, T::kDma>(myDma);
             wait_lgkmcnt<kReadsStep>();
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            issue_stage(step + STAGES - 1, 0, 1);
-            read_stage(step + 1, cur ^ 1);
+#pragma unroll
+            for (int u = 0; u < SPS; ++u)
+                issue_stage(step + STAGES - SPS + u, 0, 1);
+#pragma unroll
+            for (int u = 0; u < SPS; ++u)
+                read_stage(step + SPS + u, cur ^ 1, u);
             __builtin_amdgcn_sched_barrier(0);
-            compute_stage(cur);
+#pragma unroll
+            for (int u = 0; u < SPS; ++u)
+                if (full || step + u < steps)
+                    compute_stage(cur, u);
             __builtin_amdgcn_sched_barrier(0);
         };
 #pragma unroll
-        for (int st = 0; st < STAGES - 1; ++st)
+        for (int st = 0; st < STAGES - SPS; ++st)
             issue_stage(st, 0, 1);
-        wait_stage();
+        // the first SPS stages landed: of STAGES-SPS issued, STAGES-2SPS may be in flight
+        if constexpr (T::kEvenA && T::kEvenB)
+            wait_vmcnt<(STAGES - 2 * SPS) * T::kDma>();
+        else
+            wait_vmcnt_rt<STAGES - 2 * SPS, T::kDma>(myDma);
         __syncthreads();
-        read_stage(0, 0);
+#pragma unroll
+        for (int u = 0; u < SPS; ++u)
+            read_stage(u, 0, u);
         // both halves unconditional inside the loop, so the accumulators keep
-        // their registers across it; an odd last step runs after it
+        // their registers across it; the last one or two steps run after it
         int step = 0;
-        for (; step + 1 < steps; step += 2) {
-            one_step(step, 0);
-            one_step(step + 1, 1);
+        for (; step + 2 * SPS <= steps; step += 2 * SPS) {
+            one_step(step, 0, true);
+            one_step(step + SPS, 1, true);
         }
         if (step < steps)
-            one_step(step, 0);
+            one_step(step, 0, false);
+        if (step + SPS < steps)
+            one_step(step + SPS, 1, false);
     }
 
     // The loads issued in the last steps (zeros past K) must land before LDS
