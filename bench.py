@@ -5,9 +5,9 @@ One step is one pass of every kernel of the path over one batch of
 synthetic, HBM-resident inputs, in the order a model would run them:
 
   1. quantize_rows   fp16 fused-QKV weight [12288, 4096] -> int8 codes + fp16 scales
-  2. gemm w8a8       those codes, M = 64 (streaming path, chosen by M)
+  2. gemm w8a8       those codes, M = 64 (tiled matrix-core path, 64x64 tiles)
   3. pack_int4       int4 weight values [4096, 4096] -> [4096, 2048] bytes
-  4. gemm w4a8       decode GEMV, M = 1, N = K = 4096 (streaming path)
+  4. gemm w4a8       decode GEMV, M = 1, N = K = 4096 (dot-product GEMV path)
   5. gemm w4a8       prefill, M = 4096, N = K = 4096 (tiled matrix-core path)
   6. pack_int2       ternary weight values [4096, 4096] -> [4096, 1024] bytes
   7. gemm w2a8       ternary, M = 1 and M = 128, N = K = 4096
@@ -17,6 +17,10 @@ than twice the 256 MB Infinity Cache, so every timed read comes from HBM.
 Each kernel is timed with HIP events recorded on the stream it runs on;
 `value` is the headline: int8 TOPS of the M = 4096 W4A8 GEMM.  The decode
 GEMV's HBM GB/s and every other kernel's rate are reported under "kernels".
+After the step, "extras" times the rest of the W4A8 M sweep (M = 16, 64,
+256, 1024), the decode GEMV at N = 11008, and the rows built on the same
+kernels (per-token linear, batched QKV, fused GELU, int4 weight preparation,
+W4A16 NF4), none of which enter `value` or `ms_per_step`.
 """
 from __future__ import annotations
 
@@ -378,8 +382,52 @@ def main():
         del A_nf, C_nf
     del nf_ring, codes_nf
 
+    # The rest of the W4A8 M sweep at N = K = 4096 (M = 1 and 4096 are in the
+    # step) and the decode GEMV at N = 11008, each launch on a different
+    # packed B of a ring past the MALL, timed one launch at a time.
+    def time_launches(fn, nring):
+        for i in range(args.warmup):
+            fn(i % nring)
+        torch.cuda.synchronize()
+        evs_l = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        hold_gpu()
+        for i in range(args.steps):
+            evs_l[i][0].record()
+            fn((i + nring // 2) % nring)
+            evs_l[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs_l])) * 1e3
+
+    def perf(M_, N_, us, bits=4):
+        ops, nbytes = roofline.gemm_ops(M_, N_, K), roofline.gemm_bytes(M_, N_, K, bits)
+        b, _ = roofline.bound(ops, nbytes)
+        gbs, tops = nbytes / (us * 1e-6), ops / (us * 1e-6)
+        return {"shape": [M_, N_, K], "path": bq.select_path(M_, N_, K, bits), "us": round(us, 2),
+                "GB_per_s": round(gbs / 1e9, 1), "TOPS": round(tops / 1e12, 2), "bound": b,
+                "frac_of_bound": round(gbs / roofline.HBM_PEAK_BYTES_PER_S if b == "hbm"
+                                       else tops / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4)}
+
+    sweep = {}
+    for Ms in (16, 64, 256, 1024):
+        A_s = A4096_d[:Ms]
+        C_s = torch.empty((Ms, 4096), dtype=torch.float16, device=dev)
+        us = time_launches(lambda r: bq.gemm_w4a8_dequant(A_s, B4p_ring[r], s4_d, C_s), len(B4p_ring))
+        sweep["gemm_w4a8_m%d" % Ms] = perf(Ms, 4096, us)
+        del C_s
+    _, B11v, s11h = synth.w4a8_case(1, 11008, K, seed=0)
+    s11 = up(s11h)
+    B11 = torch.empty((11008, K // 2), dtype=torch.uint8, device=dev)
+    bq.pack_int4(up(B11v), B11)
+    del B11v
+    B11_ring = ring(B11, ring_len(B11.numel()))
+    C11 = torch.empty((1, 11008), dtype=torch.float16, device=dev)
+    us = time_launches(lambda r: bq.gemm_w4a8_dequant(A1_d, B11_ring[r], s11, C11), len(B11_ring))
+    sweep["gemm_w4a8_m1_n11008"] = perf(1, 11008, us)
+    del B11_ring, B11
+
     extras = {
         **nf4_res,
+        "w4a8_sweep": sweep,
         "weight_prep_int4": {
             "shape": list(W.shape), "quantize_us": round(prep_q_us, 2), "pack_us": round(prep_p_us, 2),
             "GB_per_s": round(prep_bytes / ((prep_q_us + prep_p_us) * 1e-6) / 1e9, 1),
