@@ -424,6 +424,19 @@ def main():
     us = time_launches(lambda r: bq.gemm_w4a8_dequant(A1_d, B11_ring[r], s11, C11), len(B11_ring))
     sweep["gemm_w4a8_m1_n11008"] = perf(1, 11008, us)
     del B11_ring, B11
+    # Decode with the three projections of a fused QKV weight in one launch:
+    # three int4 [4096, 4096] weights, one activation row broadcast to all.
+    Bqkv = torch.stack([B4p_ring[0], B4p_ring[1], B4p_ring[2]])
+    Bqkv_ring = ring(Bqkv, ring_len(Bqkv.numel()))
+    sqkv = torch.stack([s4_d, s4_d, s4_d])
+    Cqkv = torch.empty((3, 1, 4096), dtype=torch.float16, device=dev)
+    us = time_launches(lambda r: bq.gemm_batched(A1_d, Bqkv_ring[r], 4, sqkv, out=Cqkv), len(Bqkv_ring))
+    qkv1_bytes = 3 * roofline.gemm_bytes(1, 4096, K, 4) - 2 * K  # the activation row is read once
+    sweep["gemm_w4a8_m1_qkv_batched"] = {
+        "shape": [3, 1, 4096, K], "path": bq.select_path(1, 4096, K, 4), "us": round(us, 2),
+        "GB_per_s": round(qkv1_bytes / (us * 1e-6) / 1e9, 1),
+        "frac_of_bound": round(qkv1_bytes / (us * 1e-6) / roofline.HBM_PEAK_BYTES_PER_S, 4), "bound": "hbm"}
+    del Bqkv_ring, Bqkv
 
     extras = {
         **nf4_res,

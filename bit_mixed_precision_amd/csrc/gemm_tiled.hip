@@ -200,10 +200,12 @@ struct TiledCfg {
     static constexpr int kFM = kWM / 32;                // 32x32 fragments per wave along M
     static constexpr int kFN = kWN / 32;                // and N
     static constexpr int kSPR = 8 / BITS;               // sub-steps fed by one packed 16-byte read
-    // epilogue staging: 64 rows (or fewer) of kWN fp16 per wave, rows padded by 16 bytes
+    // epilogue staging: 64 rows (or fewer) of kWN outputs (fp16 or int32) per
+    // wave, rows padded by 16 bytes
+    static constexpr int kES = F16OUT ? 2 : 4;          // bytes per output element
     static constexpr int kEpiRows = kWM < 64 ? kWM : 64;
-    static constexpr int kEpiPitch = kWN * 2 + 16;
-    static constexpr int kEpiBytes = F16OUT ? WAVES * kEpiRows * kEpiPitch : 0;
+    static constexpr int kEpiPitch = kWN * kES + 16;
+    static constexpr int kEpiBytes = WAVES * kEpiRows * kEpiPitch;
     // NF4: each B row's 16 dequantized fp16 weights after the ring, rows
     // 36 bytes apart (an odd number of dwords spreads the rows over the banks)
     static constexpr int kTblPitch = 36;
@@ -729,14 +731,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // Accumulator layout (C transposed): lane l of acc[i][j] holds row
     // m = wm*kWM + 32 i + (l & 31) and, in registers 4g..4g+3, the four
     // consecutive columns n = wn*kWN + 32 j + 8 g + 4 (l >> 5) + (0..3).
-    const int mrow = wm * T::kWM + fr;
-    if constexpr (F16OUT) {
-        const bool vecN = (N % 8) == 0;
+    // Both output types are staged through LDS, 64 rows (or fewer) of each
+    // wave's tile at a time, and written as whole 16-byte chunks of rows.
+    {
+        constexpr int kPerChunk = 16 / T::kES;           // outputs per 16-byte chunk
+        const bool vecN = (N % kPerChunk) == 0;
         __syncthreads();  // every wave is done with the stage buffers
         int8_t *stg = lds + wave * T::kEpiRows * T::kEpiPitch;
-        constexpr int kChunksPerRow = T::kWN / 8;        // 16-byte chunks per staged row
+        constexpr int kChunksPerRow = T::kWN / kPerChunk;  // 16-byte chunks per staged row
         constexpr int kRowsPerIt = 64 / kChunksPerRow;
         constexpr int kFragsPerPass = T::kEpiRows / 32;
+        static_assert(kChunksPerRow <= 64 && 64 % kChunksPerRow == 0 && T::kEpiRows % kRowsPerIt == 0,
+                      "epilogue copy-out shape");
 #pragma unroll
         for (int i0 = 0; i0 < T::kFM; i0 += kFragsPerPass) {
 #pragma unroll
@@ -744,38 +750,50 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int nl = j * 32 + 8 * g + 4 * fg;  // first of 4 columns, wave-local
-                    // scale / 2^kShift folds the exact int4/int2 rescaling into
-                    // the multiply (a power-of-two factor, exact in fp32)
-                    constexpr float kInv = 1.0f / (float)(1 << U::kShift);
-                    float s[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // NF4: the scale is in the weights
-                    if constexpr (!NF4) {
-                        s[0] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x & 0xFFFF))) * kInv;
-                        s[1] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x >> 16))) * kInv;
-                        s[2] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y & 0xFFFF))) * kInv;
-                        s[3] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y >> 16))) * kInv;
-                    }
-#pragma unroll
-                    for (int ii = 0; ii < kFragsPerPass; ++ii) {
-                        const int i = i0 + ii;
-                        // weight scale, times the row's activation scale with
-                        // FUSE (a product of two fp16 values, exact in fp32),
-                        // then the activation
-                        float v[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if constexpr (NF4)
-                                v[e] = acc[i][j][4 * g + e];
-                            else
-                                v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? s[e] * xsv[i] : s[e]);
-                            if constexpr (FUSE)
-                                v[e] = apply_act(v[e], act);
+                    if constexpr (F16OUT) {
+                        // scale / 2^kShift folds the exact int4/int2 rescaling into
+                        // the multiply (a power-of-two factor, exact in fp32)
+                        constexpr float kInv = 1.0f / (float)(1 << U::kShift);
+                        float s[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // NF4: the scale is in the weights
+                        if constexpr (!NF4) {
+                            s[0] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x & 0xFFFF))) * kInv;
+                            s[1] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x >> 16))) * kInv;
+                            s[2] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y & 0xFFFF))) * kInv;
+                            s[3] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y >> 16))) * kInv;
                         }
-                        // pairs converted as two-element fp16 vectors
-                        const h2v p01 = {(_Float16)v[0], (_Float16)v[1]};
-                        const h2v p23 = {(_Float16)v[2], (_Float16)v[3]};
-                        const int r = ii * 32 + fr;
-                        *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) =
-                            make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+#pragma unroll
+                        for (int ii = 0; ii < kFragsPerPass; ++ii) {
+                            const int i = i0 + ii;
+                            // weight scale, times the row's activation scale with
+                            // FUSE (a product of two fp16 values, exact in fp32),
+                            // then the activation
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if constexpr (NF4)
+                                    v[e] = acc[i][j][4 * g + e];
+                                else
+                                    v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? s[e] * xsv[i] : s[e]);
+                                if constexpr (FUSE)
+                                    v[e] = apply_act(v[e], act);
+                            }
+                            // pairs converted as two-element fp16 vectors
+                            const h2v p01 = {(_Float16)v[0], (_Float16)v[1]};
+                            const h2v p23 = {(_Float16)v[2], (_Float16)v[3]};
+                            const int r = ii * 32 + fr;
+                            *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) =
+                                make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+                        }
+                    } else {
+                        // exact: the sums are multiples of 2^kShift
+#pragma unroll
+                        for (int ii = 0; ii < kFragsPerPass; ++ii) {
+                            const int i = i0 + ii;
+                            const int r = ii * 32 + fr;
+                            *(int4 *)(stg + r * T::kEpiPitch + nl * 4) =
+                                make_int4(acc[i][j][4 * g] >> U::kShift, acc[i][j][4 * g + 1] >> U::kShift,
+                                          acc[i][j][4 * g + 2] >> U::kShift, acc[i][j][4 * g + 3] >> U::kShift);
+                        }
                     }
                 }
             }
@@ -787,50 +805,29 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 const int c = lane % kChunksPerRow;
                 const uint4 v = *(const uint4 *)(stg + r * T::kEpiPitch + c * 16);
                 const int m = m0 + wm * T::kWM + i0 * 32 + r;
-                const int n = n0 + wn * T::kWN + c * 8;
+                const int n = n0 + wn * T::kWN + c * kPerChunk;
                 if (m < M && n < N) {
-                    __half *dst = (__half *)C + (int64_t)m * N + n;
-                    if (vecN && n + 8 <= N) {
+                    void *dst = (int8_t *)C + ((int64_t)m * N + n) * T::kES;
+                    if (vecN && n + kPerChunk <= N) {
                         *(uint4 *)dst = v;
                     } else {
                         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                        if constexpr (F16OUT) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (n + e < N)
-                                ((uint16_t *)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                            for (int e = 0; e < 8; ++e)
+                                if (n + e < N)
+                                    ((uint16_t *)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < N)
+                                    ((uint32_t *)dst)[e] = w[e];
+                        }
                     }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
-        }
-    } else {
-        const bool vecN = (N % 4) == 0;
-#pragma unroll
-        for (int i = 0; i < T::kFM; ++i) {
-            const int m = m0 + mrow + i * 32;
-            if (m >= M)
-                continue;
-#pragma unroll
-            for (int j = 0; j < T::kFN; ++j) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * T::kWN + j * 32 + 8 * g + 4 * fg;
-                    int v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = acc[i][j][4 * g + e] >> U::kShift;
-                    int *dst = (int *)C + (int64_t)m * N + n;
-                    if (vecN && n + 4 <= N) {
-                        *(int4 *)dst = make_int4(v[0], v[1], v[2], v[3]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N)
-                                dst[e] = v[e];
-                    }
-                }
-            }
         }
     }
 }
