@@ -20,7 +20,9 @@ GEMV's HBM GB/s and every other kernel's rate are reported under "kernels".
 After the step, "extras" times the rest of the W4A8 M sweep (M = 16, 64,
 256, 1024), the decode GEMV at N = 11008, and the rows built on the same
 kernels (per-token linear, batched QKV, fused GELU, int4 weight preparation,
-W4A16 NF4), none of which enter `value` or `ms_per_step`.
+W4A16 NF4), none of which enter `value` or `ms_per_step`; "ceilings" puts
+a plain device copy and the vendor library's int8 GEMM, measured in the same
+run, beside this library's kernels.
 """
 from __future__ import annotations
 
@@ -519,6 +521,55 @@ def main():
         "algorithmic_bytes": work["gemm_w4a8_m4096"]["bytes"],
     }
 
+    # Measured ceilings in the same run (box-to-box differences cancel in the
+    # ratios): a plain 512 MiB device copy (read + write bytes), and the vendor
+    # library's int8 GEMM at M = N = K = 4096 (torch._int_mm, i.e. hipBLASLt,
+    # int8 x int8 -> int32; measurement context only, not used by the path)
+    # beside this library's int8 x int8 -> int32 and W4A8 -> fp16 GEMMs, each
+    # launch timed alone between two 64 MiB copies, as in the step.
+    gap_src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    gap_dst = torch.empty_like(gap_src)
+
+    def time_alone(fn):
+        for _ in range(args.warmup):
+            fn()
+        evs_c = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        hold_gpu()
+        for i in range(args.steps):
+            gap_dst.copy_(gap_src)
+            evs_c[i][0].record()
+            fn()
+            evs_c[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs_c])) * 1e3
+
+    cp_src = torch.empty(256 << 20, dtype=torch.float16, device=dev).fill_(1.0)
+    cp_dst = torch.empty_like(cp_src)
+    copy_us = time_alone(lambda: cp_dst.copy_(cp_src))
+    copy_gbs = 2 * cp_src.numel() * 2 / (copy_us * 1e-6) / 1e9
+    del cp_src, cp_dst
+    B8 = q_ring[0][:4096]                      # int8 codes [4096, 4096]
+    C32 = torch.empty((4096, 4096), dtype=torch.int32, device=dev)
+    ops4096 = roofline.gemm_ops(4096, 4096, K)
+    vendor_us = time_alone(lambda: torch._int_mm(A4096_d, B8.t()))
+    own_i32_us = time_alone(lambda: bq.gemm_w8a8_i32(A4096_d, B8, out=C32))
+    own_w4_us = time_alone(lambda: bq.gemm_w4a8_dequant(A4096_d, B4p_ring[0], s4_d, C4096))
+    del C32, gap_src, gap_dst
+    ceilings = {
+        "device_copy_512MiB": {"us": round(copy_us, 2), "GB_per_s": round(copy_gbs, 1),
+                               "frac_of_hbm_peak": round(copy_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4)},
+        "vendor_int8_gemm_4096": {"kernel": "torch._int_mm (hipBLASLt), int8 x int8 -> int32",
+                                  "us": round(vendor_us, 2), "TOPS": round(ops4096 / (vendor_us * 1e-6) / 1e12, 2)},
+        "own_w8a8_i32_4096": {"us": round(own_i32_us, 2), "TOPS": round(ops4096 / (own_i32_us * 1e-6) / 1e12, 2),
+                              "vs_vendor": round(vendor_us / own_i32_us, 4)},
+        "own_w4a8_f16_4096": {"us": round(own_w4_us, 2), "TOPS": round(ops4096 / (own_w4_us * 1e-6) / 1e12, 2),
+                              "vs_vendor": round(vendor_us / own_w4_us, 4)},
+        "gemv_m1_sustained_vs_copy": round(
+            work["gemm_w4a8_m1"]["bytes"] / (gemv_sustained_us * 1e-6) / 1e9 / copy_gbs, 4),
+        "quantize_vs_copy": round(kernels["quantize_rows"]["GB_per_s"] / copy_gbs, 4),
+    }
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -566,6 +617,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "extras": extras,
+        "ceilings": ceilings,
     }
     print(json.dumps(line), flush=True)
 
