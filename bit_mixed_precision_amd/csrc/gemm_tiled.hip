@@ -88,17 +88,44 @@ __device__ __forceinline__ Acc mma32(const v4i &b, const v4i &a, const Acc &c)
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c, 0, 0, 0);
 }
 
-// Eight 4-bit codes (one dword, the lowest k in the low nibble) -> eight
-// fp16 weights of one B row, looked up in that row's 16-entry table in LDS.
-__device__ __forceinline__ v4i decode_nf4(uint32_t p, const uint16_t *row)
+// NF4 decode from a per-lane register table of one B row's 16 dequantized
+// fp16 weights: the low bytes of entries 4q..4q+3 in lo[q], the high bytes in
+// hi[q].  A byte permute (v_perm_b32) selects among 8 table bytes per output
+// byte, so entries 0-7 and 8-15 are selected separately and merged by the
+// code's bit 3; no LDS lookups (and no bank conflicts) on the path to the
+// matrix cores.
+struct Nf4Lut {
+    uint32_t lo[4], hi[4];
+};
+
+// Four codes (one per byte, 0..15) -> their four fp16 weights, two per dword
+// in byte order (the code in byte 0 in the low half of o01).
+__device__ __forceinline__ void nf4_lookup4(uint32_t c, const Nf4Lut &t, uint32_t &o01, uint32_t &o23)
 {
+    const uint32_t sel = c & 0x07070707u;
+    const uint32_t m8 = c & 0x08080808u;
+    const uint32_t mask = (m8 << 5) - (m8 >> 3);  // 0xFF in the bytes whose code is >= 8
+    const uint32_t lo0 = __builtin_amdgcn_perm(t.lo[1], t.lo[0], sel);
+    const uint32_t lo1 = __builtin_amdgcn_perm(t.lo[3], t.lo[2], sel);
+    const uint32_t hi0 = __builtin_amdgcn_perm(t.hi[1], t.hi[0], sel);
+    const uint32_t hi1 = __builtin_amdgcn_perm(t.hi[3], t.hi[2], sel);
+    const uint32_t lo = (lo1 & mask) | (lo0 & ~mask);
+    const uint32_t hi = (hi1 & mask) | (hi0 & ~mask);
+    o01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // lo.b0 hi.b0 lo.b1 hi.b1
+    o23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // lo.b2 hi.b2 lo.b3 hi.b3
+}
+
+// Eight 4-bit codes (one dword, the lowest k in the low nibble) -> eight
+// fp16 weights of one B row, in k order.
+__device__ __forceinline__ v4i decode_nf4(uint32_t p, const Nf4Lut &t)
+{
+    const uint32_t ev = p & 0x0F0F0F0Fu;                               // codes of k = 0, 2, 4, 6
+    const uint32_t od = (p >> 4) & 0x0F0F0F0Fu;                        // k = 1, 3, 5, 7
+    const uint32_t c03 = __builtin_amdgcn_perm(od, ev, 0x05010400u);  // k = 0, 1, 2, 3
+    const uint32_t c47 = __builtin_amdgcn_perm(od, ev, 0x07030602u);  // k = 4, 5, 6, 7
     uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = row[(p >> (8 * e)) & 15u];
-        const uint32_t hi = row[(p >> (8 * e + 4)) & 15u];
-        o[e] = lo | (hi << 16);
-    }
+    nf4_lookup4(c03, t, o[0], o[1]);
+    nf4_lookup4(c47, t, o[2], o[3]);
     return (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
 }
 
@@ -206,11 +233,7 @@ struct TiledCfg {
     static constexpr int kEpiRows = kWM < 64 ? kWM : 64;
     static constexpr int kEpiPitch = kWN * kES + 16;
     static constexpr int kEpiBytes = WAVES * kEpiRows * kEpiPitch;
-    // NF4: each B row's 16 dequantized fp16 weights after the ring, rows
-    // 36 bytes apart (an odd number of dwords spreads the rows over the banks)
-    static constexpr int kTblPitch = 36;
-    static constexpr int kTblOff = STAGES * kStage;
-    static constexpr int kRing = STAGES * kStage + (NF4 ? BN * kTblPitch : 0);
+    static constexpr int kRing = STAGES * kStage;
     static constexpr int kLds = (kRing > kEpiBytes) ? kRing : kEpiBytes;
     static_assert(kSA % 1024 == 0 && kSB % 1024 == 0, "whole 1 KB DMA blocks");
     static_assert(kLds <= 160 * 1024, "LDS");
@@ -230,8 +253,8 @@ struct TiledCfg {
 // the byte width of an A row (twice the number of k), so a stage of 128 A
 // bytes is 64 k, and the packed B row (K/4 bytes in these terms, two codes
 // per byte) has the int2 layout (BITS = 2).  `scale` is the per-row weight
-// scale and `xscale` the per-row zero point (NULL = 0): every workgroup
-// first builds its B rows' dequantized 16-entry tables in LDS,
+// scale and `xscale` the per-row zero point (NULL = 0): every lane first
+// builds the dequantized 16-entry table of each B row it feeds in registers,
 // fp16((table[c] - zero) * scale) in fp32; the matrix cores then take fp16
 // operands (v_mfma_f32_32x32x16_f16) and the fp32 sums go out as fp16.
 template <int BITS, int BM, int BN, int STAGES, bool F16OUT, bool KTAIL, int WAVES, bool FUSE, bool SPLIT,
@@ -403,28 +426,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             acc[i][j] = (Acc){};
 
     // NF4: the dequantized table of each B row this lane feeds (one per
-    // fragment column j)
-    const uint16_t *tblRow[NF4 ? T::kFN : 1];
+    // fragment column j), in registers
+    Nf4Lut lut[NF4 ? T::kFN : 1];
     if constexpr (NF4) {
-        uint16_t *tbl = (uint16_t *)(lds + T::kTblOff);
-        for (int e = tid; e < BN * 16; e += kThreads) {
-            const int r = e >> 4, c = e & 15;
-            const int n = n0 + r;
-            float w = 0.0f;
-            if (n < N) {
-                const float sc1 = __half2float(__ushort_as_half(scale[n]));
-                const float z = xscale ? __half2float(__ushort_as_half(xscale[n])) : 0.0f;
-                // two fp32 roundings, then one to fp16; the empty asm keeps the
-                // multiply from being fused with the conversion (one rounding)
-                const float d = __half2float(__ushort_as_half(kNf4TableF16[c])) - z;
-                w = d * sc1;
-                asm volatile("" : "+v"(w));
-            }
-            tbl[r * (T::kTblPitch / 2) + c] = __half_as_ushort(__float2half_rn(w));
-        }
 #pragma unroll
-        for (int j = 0; j < T::kFN; ++j)
-            tblRow[j] = tbl + (wn * T::kWN + j * 32 + fr) * (T::kTblPitch / 2);
+        for (int j = 0; j < T::kFN; ++j) {
+            const int n = n0 + wn * T::kWN + j * 32 + fr;
+            float sc1 = 0.0f, z = 0.0f;
+            if (n < N) {
+                sc1 = __half2float(__ushort_as_half(scale[n]));
+                z = xscale ? __half2float(__ushort_as_half(xscale[n])) : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // two fp32 roundings, then one to fp16; the empty asm keeps
+                    // the multiply from being fused with the conversion (one
+                    // rounding); rows past N get zero weights
+                    const float d = __half2float(__ushort_as_half(kNf4TableF16[4 * q + e])) - z;
+                    float w = d * sc1;
+                    asm volatile("" : "+v"(w));
+                    const uint32_t h = n < N ? (uint32_t)__half_as_ushort(__float2half_rn(w)) : 0u;
+                    lo |= (h & 0xFFu) << (8 * e);
+                    hi |= (h >> 8) << (8 * e);
+                }
+                lut[j].lo[q] = lo;
+                lut[j].hi[q] = hi;
+            }
+        }
     }
 
     // B operands of sub-step ks, unpacked from the packed 16-byte read that
@@ -436,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         for (int j = 0; j < T::kFN; ++j) {
             const uint4 &pk = fbp[pslot][j];
             if constexpr (NF4)
-                bop[oslot][j] = decode_nf4(dword_of(pk, tt), tblRow[j]);
+                bop[oslot][j] = decode_nf4(dword_of(pk, tt), lut[j]);
             else if constexpr (BITS == 8)
                 bop[oslot][j] = U::template operand<0>(pk);
             else if constexpr (BITS == 4)
@@ -590,7 +621,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                 for (int j = 0; j < T::kFN; ++j) {
                     if constexpr (NF4)
-                        bo[j] = decode_nf4(dword_of(gb[slot][u][0][j], ks), tblRow[j]);
+                        bo[j] = decode_nf4(dword_of(gb[slot][u][0][j], ks), lut[j]);
                     else
                         bo[j] = U::operand_rt(gb[slot][u][ks / T::kSPR][j], ks % T::kSPR);
                 }
@@ -948,12 +979,12 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 256)
         // NF4: a 1 x 8 wavefront grid (256 x 32 each), so each B column's
-        // codes are looked up by one wavefront instead of two
+        // codes are decoded by one wavefront instead of two
         return launch_t<BITS, 256, 256, kStages256, 8, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
                                                                                batch, bs, s);
     // 128 x 128: int4 eight wavefronts (2 x 4 of 64 x 32); int8 four (2 x 2
     // of 64 x 64); int2 and NF4 four in a 1 x 4 grid (128 x 32 each), so each
-    // B column is unpacked or looked up by one wavefront
+    // B column is unpacked or decoded by one wavefront
     constexpr int kWaves128 = BITS == 4 ? 8 : 4;
     constexpr int kWgm128 = BITS == 2 ? 1 : 2;
     // 64 x 64: four wavefronts (2 x 2 of 32 x 32); NF4 two (1 x 2 of 64 x 32)
