@@ -122,7 +122,9 @@ def main():
 
     from bit_mixed_precision_amd import bq, roofline, synth
 
-    if not os.path.exists(bq.LIB_PATH):
+    from bit_mixed_precision_amd import _build as lib_build
+
+    if not os.path.exists(bq.LIB_PATH) or not os.path.exists(lib_build.CALIB_LIB):
         import __graft_entry__
 
         __graft_entry__.build()
@@ -555,8 +557,43 @@ def main():
     vendor_us = time_alone(lambda: torch._int_mm(A4096_d, B8.t()))
     own_i32_us = time_alone(lambda: bq.gemm_w8a8_i32(A4096_d, B8, out=C32))
     own_w4_us = time_alone(lambda: bq.gemm_w4a8_dequant(A4096_d, B4p_ring[0], s4_d, C4096))
-    del C32, gap_src, gap_dst
+    # Achievable ceilings of the box itself (libbq_calib.so, measurement
+    # kernels only): int8 matrix-core instructions on register operands
+    # (1024 workgroups of four wavefronts, four independent accumulators
+    # each), and a plain streaming read of 1 GiB.
+    import ctypes
+
+    calib = ctypes.CDLL(lib_build.CALIB_LIB)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cal_out = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    loop_blocks, loop_iters = 1024, 4000
+
+    def mfma_loop():
+        rc = calib.bq_calib_mfma_loop(loop_blocks, loop_iters, ctypes.c_void_p(cal_out.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"bq_calib_mfma_loop: hip error {rc}")
+
+    rd_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+
+    def read_stream():
+        rc = calib.bq_calib_read_stream(ctypes.c_void_p(rd_buf.data_ptr()), ctypes.c_int64(rd_buf.numel()), 2048,
+                                        ctypes.c_void_p(cal_out.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"bq_calib_read_stream: hip error {rc}")
+
+    loop_us = time_alone(mfma_loop)
+    loop_tops = loop_blocks * 4 * loop_iters * 4 * 65536 / (loop_us * 1e-6) / 1e12
+    read_us = time_alone(read_stream)
+    read_gbs = rd_buf.numel() / (read_us * 1e-6) / 1e9
+    del rd_buf, cal_out, C32, gap_src, gap_dst
+    gemv_sus_gbs = work["gemm_w4a8_m1"]["bytes"] / (gemv_sustained_us * 1e-6) / 1e9
     ceilings = {
+        "mfma_i8_loop": {"us": round(loop_us, 2), "TOPS": round(loop_tops, 2),
+                         "frac_of_int8_peak": round(loop_tops * 1e12 / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4)},
+        "read_stream_1GiB": {"us": round(read_us, 2), "GB_per_s": round(read_gbs, 1),
+                             "frac_of_hbm_peak": round(read_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4)},
+        "value_frac_of_mfma_loop": round(head_tops / loop_tops, 4),
+        "gemv_m1_sustained_frac_of_read_stream": round(gemv_sus_gbs / read_gbs, 4),
         "device_copy_512MiB": {"us": round(copy_us, 2), "GB_per_s": round(copy_gbs, 1),
                                "frac_of_hbm_peak": round(copy_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4)},
         "vendor_int8_gemm_4096": {"kernel": "torch._int_mm (hipBLASLt), int8 x int8 -> int32",

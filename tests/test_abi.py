@@ -162,3 +162,18 @@ def test_nf4_validation(bq):
     assert f(P16, PODD, P16c, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_ALIGN
     assert f(NULL, NULL, NULL, NULL, NULL, 0, 4, 64, S) == bq.BQ_OK
     assert f(NULL, NULL, NULL, NULL, NULL, 4, 0, 64, S) == bq.BQ_OK
+
+
+def test_calib_library_exports(bq):
+    """The benchmark's measurement kernels (libbq_calib.so) load and export
+    their two entry points; argument checks run on the host."""
+    from bit_mixed_precision_amd import _build
+
+    if not os.path.exists(_build.CALIB_LIB):
+        _build.build_calib()
+    lib = ctypes.CDLL(_build.CALIB_LIB)
+    for name in ("bq_calib_mfma_loop", "bq_calib_read_stream"):
+        assert hasattr(lib, name), name
+    # invalid arguments are rejected before any launch (no GPU needed)
+    assert lib.bq_calib_mfma_loop(0, 1, None, None) != 0
+    assert lib.bq_calib_read_stream(None, ctypes.c_int64(16), 1, None, None) != 0
