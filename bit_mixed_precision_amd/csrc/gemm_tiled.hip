@@ -230,8 +230,9 @@ struct TiledCfg {
     // epilogue staging: 64 rows (or fewer) of kWN outputs (fp16 or int32) per
     // wave, rows padded by 16 bytes
     static constexpr int kES = F16OUT ? 2 : 4;          // bytes per output element
-    static constexpr int kEpiRows = kWM < 64 ? kWM : 64;
     static constexpr int kEpiPitch = kWN * kES + 16;
+    // 64 rows per pass, or 32 where 64 rows of every wave's tile would not fit in LDS
+    static constexpr int kEpiRows = kWM < 64 ? kWM : WAVES * 64 * kEpiPitch <= 160 * 1024 ? 64 : 32;
     static constexpr int kEpiBytes = WAVES * kEpiRows * kEpiPitch;
     static constexpr int kRing = STAGES * kStage;
     static constexpr int kLds = (kRing > kEpiBytes) ? kRing : kEpiBytes;
