@@ -45,7 +45,7 @@ HOLD_CYCLES = 50_000_000
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline sample")
@@ -503,9 +503,11 @@ def main():
         b, _ = roofline.bound(w["ops"], w["bytes"])
         gbs = w["bytes"] / t / 1e9
         tops = w["ops"] / t / 1e12
+        p10, p50, p90 = np.percentile(dur_ms[:, j] * 1e3, [10, 50, 90])
         kernels[n] = {
             "shape": w["shape"], "us": round(mean_ms[j] * 1e3, 2),
             "us_min": round(dur_ms[:, j].min() * 1e3, 2),
+            "us_p10": round(float(p10), 2), "us_p50": round(float(p50), 2), "us_p90": round(float(p90), 2),
             "GB_per_s": round(gbs, 1), "TOPS": round(tops, 2), "bound": b,
             "frac_of_bound": round(gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S if b == "hbm"
                                    else tops * 1e12 / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4),
@@ -619,8 +621,12 @@ def main():
         kernels[n]["path"] = kernel_path[n]
 
     cpu = None
+    cpu_configs = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(A4096, B4v, s4, args.cpu_seconds)
+        gpu_us = {k: v["us"] for k, v in kernels.items()}
+        gpu_us["gemm_w4a8_m1_n11008"] = sweep["gemm_w4a8_m1_n11008"]["us"]
+        cpu_configs = cpu_oracle_configs(W, A64, A1, B4v, A2, B2v, s4, s2, gpu_us)
 
     line = {
         "metric": METRIC,
@@ -652,6 +658,7 @@ def main():
             "us": round(big_sustained_us, 2),
             "TOPS": round(work["gemm_w4a8_m4096"]["ops"] / (big_sustained_us * 1e-6) / 1e12, 2)},
         "cpu_baseline": cpu,
+        "cpu_oracle_configs": cpu_configs,
         "kernels": kernels,
         "extras": extras,
         "ceilings": ceilings,
@@ -689,6 +696,41 @@ def cpu_baseline(A, Bv, s, budget_s):
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": f"{rows} of {A.shape[0]} rows of A (M={rows}, N={Bv.shape[0]}, K={Bv.shape[1]}, "
                       f"w4a8 dequant) x {reps}, {t:.1f} s"}
+
+
+def cpu_oracle_configs(W, A64, A1, B4v, A2, B2v, s4, s2, gpu_us):
+    """The oracle (as it stands, all host cores) on the other workloads of the
+    step, each timed once beside the GPU kernel's in-step time."""
+    import oracle
+
+    from bit_mixed_precision_amd import synth
+
+    out = {}
+
+    def timed(name, fn, extra=""):
+        t = time.perf_counter()
+        fn()
+        ms = (time.perf_counter() - t) * 1e3
+        g = gpu_us.get(name)
+        out[name] = {"oracle_ms": round(ms, 2), "gpu_us": g,
+                     "speedup": round(ms * 1e3 / g, 1) if g else None}
+        if extra:
+            out[name]["note"] = extra
+
+    codes = {}
+    timed("quantize_rows", lambda: codes.update(zip(("q", "s"), oracle.quantize_rows(W))))
+    timed("gemm_w8a8_m64", lambda: oracle.gemm_wxa8_dequant(A64, codes["q"], codes["s"], 8))
+    B4p = oracle.pack_int4(B4v)
+    B2p = oracle.pack_int2(B2v)
+    timed("pack_int4", lambda: oracle.pack_int4(B4v))
+    timed("gemm_w4a8_m1", lambda: oracle.gemm_wxa8_dequant(A1, B4p, s4, 4))
+    timed("pack_int2", lambda: oracle.pack_int2(B2v))
+    timed("gemm_w2a8_m1", lambda: oracle.gemm_wxa8_dequant(np.ascontiguousarray(A2[:1]), B2p, s2, 2))
+    timed("gemm_w2a8_m128", lambda: oracle.gemm_wxa8_dequant(A2, B2p, s2, 2))
+    _, B11v, s11 = synth.w4a8_case(1, 11008, W.shape[1], seed=0)
+    B11p = oracle.pack_int4(B11v)
+    timed("gemm_w4a8_m1_n11008", lambda: oracle.gemm_wxa8_dequant(A1, B11p, s11, 4))
+    return out
 
 
 if __name__ == "__main__":
