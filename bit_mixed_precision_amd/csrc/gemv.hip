@@ -5,9 +5,9 @@
 // At M <= 4 every byte of B is used by at most 4 multiply-adds, so the kernel
 // is a stream over B and its speed is set by how fast B leaves HBM.  It is
 // laid out like a plain streaming read:
-//  * one wavefront per ROWS rows of B; its 64 lanes walk the packed row in
-//    16-byte chunks (lane l takes chunks l, l+64, ...), so one load
-//    instruction covers 1 KB of a row;
+//  * one wavefront per ROWS (1 or 2) rows of B; its 64 lanes walk the
+//    packed row in 16-byte chunks (lane l takes chunks l, l+64, ...), so one
+//    load instruction covers 1 KB of a row;
 //  * all of a lane's chunk loads (for every row) are issued before any is
 //    used; the matching bytes of A (at most 4 rows, a few KB) come from the
 //    L1/L2 caches, fetched in the same batch;
@@ -157,11 +157,19 @@ template <int BITS>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale, int act,
                        void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
 {
-    // a lane's loads per batch: 2 rows x U chunks of B (64 B of packed B per
-    // row at U = 4 / 2 / 1 for 8 / 4 / 2 bits: one batch covers K = 4096)
+    // a lane's loads per batch: ROWS rows x U chunks of B (64 B of packed B
+    // per row at U = 4 / 2 / 1 for 8 / 4 / 2 bits: one batch covers K = 4096)
     constexpr int U = BITS == 8 ? 4 : BITS == 4 ? 2 : 1;
-    if (M == 1)
+    // M = 1: one B row per wavefront for int8 at any N and for int4 / int2
+    // up to 6144 rows in all (more, smaller wavefronts start streaming
+    // sooner), two above that (fewer wavefronts to launch).  Measured back to
+    // back at K = 4096: int4 N = 4096 3.94 against 4.17 us, N = 11008 7.2
+    // against 6.4 us; int8 one row is ahead at every N from 1024 to 14336.
+    if (M == 1) {
+        if (BITS == 8 || (int64_t)N * batch <= 6144)
+            return launch_t<BITS, 1, 1, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
         return launch_t<BITS, 1, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    }
     if (M == 2)
         return launch_t<BITS, 2, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     return launch_t<BITS, 4, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
