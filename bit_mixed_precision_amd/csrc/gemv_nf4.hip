@@ -5,9 +5,9 @@
 // sum accumulated in fp32 (BitBLAS custom-operator guide, case 2).
 //
 // Like the integer GEMV, this is a stream over B (four bits per weight):
-//  * one wavefront per ROWS rows of B; its lanes walk the packed row in
-//    16-byte chunks (32 codes), lane l taking chunks l, l + 64, ...; all of a
-//    lane's chunk loads of a batch are issued before any is used;
+//  * one wavefront per ROWS (1 or 2) rows of B; its lanes walk the packed
+//    row in 16-byte chunks (32 codes), lane l taking chunks l, l + 64, ...;
+//    all of a lane's chunk loads of a batch are issued before any is used;
 //  * each wavefront first builds, for each of its rows, a 256-entry table in
 //    LDS mapping a packed byte (two codes) to the two dequantized fp16
 //    weights, so one 4-byte LDS read decodes two weights;
@@ -151,12 +151,12 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(
         }
 }
 
-template <int MR>
+template <int MR, int kRows>
 hipError_t launch_t(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero, uint16_t *C,
                     int M, int N, int K, hipStream_t s)
 {
-    // 2 rows x 2 chunks of 16 bytes per lane per batch: one batch covers K = 4096
-    constexpr int kRows = 2, kU = 2;
+    // kRows rows x 2 chunks of 16 bytes per lane per batch: one batch covers K = 4096
+    constexpr int kU = 2;
     const int waves = (N + kRows - 1) / kRows;
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     gemv_nf4_kernel<MR, kRows, kU><<<grid, kThreads, 0, s>>>(A, B, scale, zero, C, M, N, K);
@@ -170,11 +170,15 @@ hipError_t launch_gemv_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *
 {
     if (M == 0 || N == 0)
         return hipSuccess;
+    // M = 1: one B row per wavefront up to N = 6144, two above (as for the
+    // integer GEMV; back to back at K = 4096: N = 4096 5.38 against 5.64 us,
+    // N = 11008 11.3 against 9.6 us)
     if (M == 1)
-        return launch_t<1>(A, B, scale, zero, C, M, N, K, s);
+        return N <= 6144 ? launch_t<1, 1>(A, B, scale, zero, C, M, N, K, s)
+                         : launch_t<1, 2>(A, B, scale, zero, C, M, N, K, s);
     if (M == 2)
-        return launch_t<2>(A, B, scale, zero, C, M, N, K, s);
-    return launch_t<4>(A, B, scale, zero, C, M, N, K, s);
+        return launch_t<2, 2>(A, B, scale, zero, C, M, N, K, s);
+    return launch_t<4, 2>(A, B, scale, zero, C, M, N, K, s);
 }
 
 }  // namespace bq
