@@ -428,6 +428,16 @@ def main():
     us = time_launches(lambda r: bq.gemm_w4a8_dequant(A1_d, B11_ring[r], s11, C11), len(B11_ring))
     sweep["gemm_w4a8_m1_n11008"] = perf(1, 11008, us)
     del B11_ring, B11
+    # The small W4A8 case, M = 16, N = 256, K = 256 (launch-bound: time only).
+    A0, B0v, s0 = synth.w4a8_case(16, 256, 256, seed=0)
+    A0_d, s0_d = up(A0), up(s0)
+    B0 = torch.empty((256, 128), dtype=torch.uint8, device=dev)
+    bq.pack_int4(up(B0v), B0)
+    C0 = torch.empty((16, 256), dtype=torch.float16, device=dev)
+    us = time_launches(lambda r: bq.gemm_w4a8_dequant(A0_d, B0, s0_d, C0), 1)
+    sweep["gemm_w4a8_16x256x256"] = {"shape": [16, 256, 256], "path": bq.select_path(16, 256, 256, 4),
+                                     "us": round(us, 2), "bound": "launch"}
+    del A0_d, B0, C0
     # Decode with the three projections of a fused QKV weight in one launch:
     # three int4 [4096, 4096] weights, one activation row broadcast to all.
     Bqkv = torch.stack([B4p_ring[0], B4p_ring[1], B4p_ring[2]])
