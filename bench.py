@@ -348,6 +348,22 @@ def main():
     prep_q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in prep_ev])) * 1e3
     prep_p_us = float(np.mean([e[1].elapsed_time(e[2]) for e in prep_ev])) * 1e3
     prep_bytes = roofline.quantize_bytes(*W.shape) + roofline.pack_bytes(W.shape[0], W.shape[1], 4)
+    # the same preparation in one pass (bq_quantize_pack): fp16 read once,
+    # packed bytes and scales written once
+    p4f = torch.empty_like(p4)
+    s4f = torch.empty_like(s4q)
+    for i in range(args.warmup):
+        bq.quantize_pack(W_d[i % len(W_d)], 4, p4f, s4f)
+    fused_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    hold_gpu()
+    for i in range(args.steps):
+        fused_ev[i][0].record()
+        bq.quantize_pack(W_d[i % len(W_d)], 4, p4f, s4f)
+        fused_ev[i][1].record()
+    torch.cuda.synchronize()
+    fused_us = float(np.mean([e[0].elapsed_time(e[1]) for e in fused_ev])) * 1e3
+    fused_bytes = W.size * 2 + W.size // 2 + 2 * W.shape[0]
 
     # W4A16 with NF4 weight codes, per-row scale and zero point: decode
     # (M = 1, a stream over the codes, bound by HBM) and prefill (M = 4096,
@@ -460,6 +476,9 @@ def main():
             "GB_per_s": round(prep_bytes / ((prep_q_us + prep_p_us) * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(prep_bytes / ((prep_q_us + prep_p_us) * 1e-6)
                                       / roofline.HBM_PEAK_BYTES_PER_S, 4),
+            "fused_us": round(fused_us, 2),
+            "fused_GB_per_s": round(fused_bytes / (fused_us * 1e-6) / 1e9, 1),
+            "fused_frac_of_hbm_peak": round(fused_bytes / (fused_us * 1e-6) / roofline.HBM_PEAK_BYTES_PER_S, 4),
         },
         "gemm_w4a8_m4096_gelu": {
             "shape": [4096, 4096, 4096], "us": round(gelu_us, 2),

@@ -41,6 +41,7 @@ SIGNATURES = {
     "bq_gemm_batched": [_P, _I64, _P, _I64, _I, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _P],
     "bq_gemm_act": [_P, _P, _I, _P, _P, _I, _P, _I64, _I64, _I64, _I, _P],
     "bq_quantize_rows_bits": [_P, _I64, _I64, _I, _P, _P, _P],
+    "bq_quantize_pack": [_P, _I64, _I64, _I, _P, _P, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
     "bq_gemm_nf4_a16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P],
 }
@@ -161,6 +162,31 @@ def quantize_rows_bits(x: torch.Tensor, bits: int, q: Optional[torch.Tensor] = N
     _check_tensor(scale, "scale", torch.float16, (rows,), dev)
     _call("bq_quantize_rows_bits", dev, _ptr(x), rows, cols, bits, _ptr(q), _ptr(scale))
     return q, scale
+
+
+def quantize_pack(x: torch.Tensor, bits: int, out: Optional[torch.Tensor] = None,
+                  scale: Optional[torch.Tensor] = None):
+    """Per-row quantization of fp16 x [rows, cols] to the int4 (bits 4) or
+    ternary (bits 2) code range, written packed -> (packed uint8 [rows,
+    cols*bits/8], scale fp16 [rows]); equal to quantize_rows_bits followed by
+    pack_int4 / pack_int2, in one pass."""
+    if bits not in (4, 2):
+        raise ValueError("bits must be 4 or 2")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if cols % (8 // bits):
+        raise ValueError(f"cols must be a multiple of {8 // bits}")
+    _check_tensor(x, "x", torch.float16)
+    dev = x.device
+    if out is None:
+        out = torch.empty((rows, cols * bits // 8), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float16, device=dev)
+    _check_tensor(out, "out", torch.uint8, (rows, cols * bits // 8), dev)
+    _check_tensor(scale, "scale", torch.float16, (rows,), dev)
+    _call("bq_quantize_pack", dev, _ptr(x), rows, cols, bits, _ptr(out), _ptr(scale))
+    return out, scale
 
 
 def _pack(name: str, factor: int, v: torch.Tensor, out: Optional[torch.Tensor]):

@@ -137,6 +137,26 @@ int bq_quantize_rows_bits(const void *x_f16, int64_t rows, int64_t cols, int bit
     return quantize_common(x_f16, rows, cols, (1 << (bits - 1)) - 1, q, scale_f16, stream);
 }
 
+int bq_quantize_pack(const void *x_f16, int64_t rows, int64_t cols, int bits, uint8_t *packed,
+                     void *scale_f16, void *stream)
+{
+    if (bits != 4 && bits != 2)
+        return BQ_ERR_ARG;
+    if (rows < 0 || cols < 0 || rows > INT32_MAX || (cols % (8 / bits)) != 0)
+        return BQ_ERR_SHAPE;
+    if (rows == 0)
+        return BQ_OK;
+    if (!scale_f16 || (cols > 0 && (!x_f16 || !packed)))
+        return BQ_ERR_NULL;
+    if (!aligned16(scale_f16) || (cols > 0 && (!aligned16(x_f16) || !aligned16(packed))))
+        return BQ_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != BQ_OK)
+        return dev;
+    return launch_status(bq::launch_quantize_pack((const uint16_t *)x_f16, rows, cols, bits, packed,
+                                                  (uint16_t *)scale_f16, (hipStream_t)stream));
+}
+
 static int pack_common(const int8_t *v, int64_t n, int64_t k, uint8_t *out, int factor)
 {
     if (n < 0 || k < 0 || (k % factor) != 0)

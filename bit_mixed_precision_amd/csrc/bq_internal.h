@@ -25,6 +25,10 @@ __device__ __forceinline__ uint4 load_nt16(const void *p)
 // Codes in [-qmax, qmax], scale = fp16(absmax / qmax); 1 <= qmax <= 127.
 hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int qmax,
                                 int8_t *q, uint16_t *scale, hipStream_t s);
+// The codes of launch_quantize_rows with qmax = 7 (bits 4) or 1 (bits 2),
+// written packed like launch_pack_int4 / launch_pack_int2; cols % (8 / bits) == 0.
+hipError_t launch_quantize_pack(const uint16_t *x, int64_t rows, int64_t cols, int bits, uint8_t *packed,
+                                uint16_t *scale, hipStream_t s);
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 

@@ -169,6 +169,99 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_any(
         qr[k] = rs.zero ? 0 : (int8_t)code_of(half_bits_to_float(xr[k]), rs.s, rs.r, rs.hs, rs.qmax);
 }
 
+// Fused quantize + pack (int4 / ternary weight preparation): the codes of
+// the row rule above with qmax = 7 or 1, written straight in the packed
+// storage of bq_pack_int4 / bq_pack_int2 (BitBLAS custom-operator guide,
+// cases 1-2: int4 two per byte, low nibble = even k; int2 code v+2 four per
+// byte, lowest bits = lowest k), so the int8 codes never go to memory.
+
+// Four int8 codes (byte i = code of k = i) -> their packed bits in the low
+// 16 (int4) or 8 (int2) bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack4(uint32_t c)
+{
+    if constexpr (BITS == 4) {
+        const uint32_t n = c & 0x0F0F0F0Fu;  // two's complement nibbles
+        const uint32_t t = n | (n >> 4);    // byte 0: k0 | k1 << 4, byte 2: k2 | k3 << 4
+        return (t & 0xFFu) | ((t >> 8) & 0xFF00u);
+    } else {
+        const uint32_t x = (c & 0x03030303u) ^ 0x02020202u;  // code v + 2 (v in [-2, 1])
+        return (x | (x >> 6) | (x >> 12) | (x >> 18)) & 0xFFu;
+    }
+}
+
+// Vector path: cols % 8 == 0; thread t owns 8-element vectors t, t+256, ...
+// and writes their 4 (int4) or 2 (int2) packed bytes.
+template <int VPT, int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_pack_vec(
+    const uint4 *__restrict__ x, int64_t cols, uint8_t *__restrict__ packed, uint16_t *__restrict__ scale)
+{
+    __shared__ uint32_t red[4];
+    const int64_t row = blockIdx.x;
+    const int nvec = (int)(cols >> 3);
+    const uint4 *xr = x + row * nvec;
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+
+    uint4 v[VPT];
+    uint32_t m2 = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int idx = threadIdx.x + j * kThreads;
+        v[j] = (idx < nvec) ? load_nt16(xr + idx) : make_uint4(0, 0, 0, 0);
+        m2 = absmax2(m2, v[j].x);
+        m2 = absmax2(m2, v[j].y);
+        m2 = absmax2(m2, v[j].z);
+        m2 = absmax2(m2, v[j].w);
+    }
+    const uint32_t amax = block_absmax(max(m2 & 0xFFFF, m2 >> 16), red);
+    const RowScale rs = row_scale(amax, qmax, scale + row);
+
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int idx = threadIdx.x + j * kThreads;
+        if (idx < nvec) {
+            const uint32_t c0 = rs.zero ? 0u : codes4(v[j].x, v[j].y, rs);
+            const uint32_t c1 = rs.zero ? 0u : codes4(v[j].z, v[j].w, rs);
+            if constexpr (BITS == 4) {
+                uint32_t *dst = (uint32_t *)(packed + row * (cols >> 1)) + idx;
+                __builtin_nontemporal_store(pack4<4>(c0) | (pack4<4>(c1) << 16), dst);
+            } else {
+                uint16_t *dst = (uint16_t *)(packed + row * (cols >> 2)) + idx;
+                __builtin_nontemporal_store((uint16_t)(pack4<2>(c0) | (pack4<2>(c1) << 8)), dst);
+            }
+        }
+    }
+}
+
+// General path (cols a multiple of 8 / BITS only): thread t owns packed
+// bytes t, t+256, ...; the row is read twice (absmax, then codes).
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_pack_any(
+    const uint16_t *__restrict__ x, int64_t cols, uint8_t *__restrict__ packed, uint16_t *__restrict__ scale)
+{
+    __shared__ uint32_t red[4];
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+    constexpr int per = 8 / BITS;  // codes per byte
+    const int64_t row = blockIdx.x;
+    const uint16_t *xr = x + row * cols;
+    uint32_t m = 0;
+    for (int64_t k = threadIdx.x; k < cols; k += kThreads)
+        m = max(m, (uint32_t)(xr[k] & 0x7FFF));
+    const uint32_t amax = block_absmax(m, red);
+    const RowScale rs = row_scale(amax, qmax, scale + row);
+    const int64_t nbytes = cols / per;
+    uint8_t *pr = packed + row * nbytes;
+    for (int64_t b = threadIdx.x; b < nbytes; b += kThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < per; ++j) {
+            const int q = rs.zero ? 0 : code_of(half_bits_to_float(xr[b * per + j]), rs.s, rs.r, rs.hs, rs.qmax);
+            c |= (uint32_t)(q & 0xFF) << (8 * j);
+        }
+        pr[b] = (uint8_t)pack4<BITS>(c);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, int qmax,
@@ -189,6 +282,38 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, i
         quantize_rows_vec<8><<<grid, block, 0, s>>>((const uint4 *)x, cols, qmax, (uint2 *)q, scale);
     else
         quantize_rows_any<<<grid, block, 0, s>>>(x, cols, qmax, q, scale);
+    return hipGetLastError();
+}
+
+}  // namespace bq
+
+namespace bq {
+
+hipError_t launch_quantize_pack(const uint16_t *x, int64_t rows, int64_t cols, int bits, uint8_t *packed,
+                                uint16_t *scale, hipStream_t s)
+{
+    if (rows == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)rows), block(kThreads);
+    const int64_t nvec = cols / 8;
+    const bool vec = (cols % 8 == 0) && cols > 0 && nvec <= 8 * kThreads;
+#define BQ_QP(BITS_)                                                                                    \
+    if (!vec)                                                                                           \
+        quantize_pack_any<BITS_><<<grid, block, 0, s>>>(x, cols, packed, scale);                       \
+    else if (nvec <= kThreads)                                                                          \
+        quantize_pack_vec<1, BITS_><<<grid, block, 0, s>>>((const uint4 *)x, cols, packed, scale);     \
+    else if (nvec <= 2 * kThreads)                                                                      \
+        quantize_pack_vec<2, BITS_><<<grid, block, 0, s>>>((const uint4 *)x, cols, packed, scale);     \
+    else if (nvec <= 4 * kThreads)                                                                      \
+        quantize_pack_vec<4, BITS_><<<grid, block, 0, s>>>((const uint4 *)x, cols, packed, scale);     \
+    else                                                                                                \
+        quantize_pack_vec<8, BITS_><<<grid, block, 0, s>>>((const uint4 *)x, cols, packed, scale);
+    if (bits == 4) {
+        BQ_QP(4)
+    } else {
+        BQ_QP(2)
+    }
+#undef BQ_QP
     return hipGetLastError();
 }
 

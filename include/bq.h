@@ -123,6 +123,24 @@ int bq_quantize_rows_bits(const void *x_f16, int64_t rows, int64_t cols, int bit
                           void *scale_f16, void *stream);
 
 /*
+ * bq_quantize_pack - bq_quantize_rows_bits (bits 4 or 2) with the codes
+ * written straight in the packed storage of bq_pack_int4 / bq_pack_int2
+ * (BMINF page, 實現代碼分析2, per-row rule with the int4 / ternary code range;
+ * BitBLAS guide, cases 1-2, packed weight storage): one pass over the fp16
+ * weight, no int8 codes in memory.  The packed bytes and scales equal those
+ * of bq_quantize_rows_bits followed by bq_pack_int4 / bq_pack_int2.
+ *
+ *   x_f16     [rows, cols] fp16 input
+ *   bits      4 or 2 (BQ_ERR_ARG otherwise)
+ *   packed    [rows, cols*bits/8] uint8 output
+ *   scale_f16 [rows] fp16 output, fp16(absmax_row / qmax), qmax = 7 or 1
+ * cols must be a multiple of 8/bits (BQ_ERR_SHAPE otherwise); rows, cols >= 0;
+ * x, packed and scale 16-byte aligned.  Other errors as bq_quantize_rows.
+ */
+int bq_quantize_pack(const void *x_f16, int64_t rows, int64_t cols, int bits, uint8_t *packed,
+                     void *scale_f16, void *stream);
+
+/*
  * bq_pack_int4 - pack int4 values held one per int8 into bytes along K.
  * BitBLAS guide, case 2 (uint8 [N, K/2] compressed storage); bit order:
  * byte [n, k/2] = (v[n,k] & 0xF) | (v[n,k+1] & 0xF) << 4 for even k.

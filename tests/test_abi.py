@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -104,6 +104,20 @@ def test_quantize_bits_validation(bq):
     assert L.bq_quantize_rows_bits(P16, 4, 64, 4, P16b, NULL, S) == bq.BQ_ERR_NULL
     assert L.bq_quantize_rows_bits(PODD, 4, 64, 4, P16b, P16c, S) == bq.BQ_ERR_ALIGN
     assert L.bq_quantize_rows_bits(NULL, 0, 64, 2, NULL, NULL, S) == bq.BQ_OK
+
+
+def test_quantize_pack_validation(bq):
+    L = bq.lib()
+    S = NULL
+    for bits in (0, 1, 3, 8):
+        assert L.bq_quantize_pack(P16, 4, 64, bits, P16b, P16c, S) == bq.BQ_ERR_ARG
+    assert L.bq_quantize_pack(P16, -1, 64, 4, P16b, P16c, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_quantize_pack(P16, 4, 63, 4, P16b, P16c, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_quantize_pack(P16, 4, 66, 2, P16b, P16c, S) == bq.BQ_ERR_SHAPE
+    assert L.bq_quantize_pack(P16, 4, 64, 4, P16b, NULL, S) == bq.BQ_ERR_NULL
+    assert L.bq_quantize_pack(P16, 4, 64, 2, NULL, P16c, S) == bq.BQ_ERR_NULL
+    assert L.bq_quantize_pack(PODD, 4, 64, 4, P16b, P16c, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_quantize_pack(NULL, 0, 64, 2, NULL, NULL, S) == bq.BQ_OK
 
 
 def test_act_validation(bq):

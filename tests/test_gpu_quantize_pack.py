@@ -176,3 +176,57 @@ def test_fp16_to_int4_gemm_flow(dev):
     ref = oracle.gemm_wxa8_dequant(A, oracle.pack_int4(q_ref), s_ref, 4)
     from gpu_util import assert_f16_within_1ulp
     assert_f16_within_1ulp(f16_bits(C), ref, "int4 flow")
+
+
+def _quantize_pack_case(dev, x16: np.ndarray, bits: int, what: str):
+    """bq_quantize_pack against the oracle's quantize_rows_bits then pack,
+    bit for bit (packed bytes and scales)."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner(f"quantize_pack bits={bits} {what} shape={x16.shape}")
+    p, s = bq.quantize_pack(to_dev(x16, dev), bits)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows_bits(x16, bits)
+    p_ref = oracle.pack_int4(q_ref) if bits == 4 else oracle.pack_int2(q_ref)
+    assert np.array_equal(f16_bits(s), s_ref), f"{what}: scales differ"
+    pg = p.cpu().numpy()
+    if not np.array_equal(pg, p_ref):
+        bad = np.argwhere(pg != p_ref)
+        r, b = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} packed bytes differ, first at {(r, b)}: "
+                             f"got {pg[r, b]:#04x} want {p_ref[r, b]:#04x}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("shape", [(3, 4), (5, 8), (7, 12), (9, 1000), (4, 4096), (6, 2056), (2, 16392),
+                                   (2, 16384), (300, 64)])
+def test_quantize_pack_shapes(dev, bits, shape):
+    g = np.random.default_rng(shape[0] * 11 + shape[1] + bits)
+    x = (g.standard_normal(shape) * np.exp(g.uniform(-6, 6, (shape[0], 1)))).astype(np.float16)
+    _quantize_pack_case(dev, x, bits, "random")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_quantize_pack_special_rows(dev, bits):
+    """Zero, underflowing and subnormal-scale rows, exact ties, the fp16 range
+    (vector path, 16 columns) and the same rows at 12 columns (general path)."""
+    qmax = (1 << (bits - 1)) - 1
+    q = 2.0 ** -24
+    rows = np.zeros((5, 16), np.float64)
+    rows[1, :4] = [q, -q, 0, 0]
+    rows[2, :4] = [40 * q, -40 * q, 7 * q, q]
+    s0 = 2.0 ** -3
+    rows[3, 0] = qmax * s0
+    halves = np.arange(-qmax, qmax) + 0.5
+    rows[3, 1:1 + len(halves)] = halves * s0
+    rows[4, :] = np.linspace(-65504, 65504, 16)
+    _quantize_pack_case(dev, rows.astype(np.float16), bits, "special rows")
+    _quantize_pack_case(dev, np.ascontiguousarray(rows[:, :12]).astype(np.float16), bits, "special rows, 12 cols")
+
+
+def test_quantize_pack_bminf_weight(dev):
+    """The fused-QKV fp16 weight [12288, 4096] to int4 in one pass, compared in
+    full with the oracle's two steps."""
+    W = synth.bminf_weight(rows=12288, cols=4096, seed=0)
+    _quantize_pack_case(dev, W, 4, "bminf weight")
