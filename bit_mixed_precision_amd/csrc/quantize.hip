@@ -19,7 +19,9 @@
 // while x*r is within 190 * 2^-23 of the quotient; q0 is then exact.  For
 // an exact half-integer (a tie) the residual e = x - q0*scale, computed
 // exactly by one fma (q0*scale has at most 19 significant bits), equals
-// +-scale/2, and q0 is moved to the even neighbour if it is odd.
+// +-scale/2, and q0 is moved to the even neighbour if it is odd (the vector
+// paths do this in float: q0 + copysign(1/2, e) is then exactly the tie and
+// its round-to-nearest-even is the even neighbour).
 // The scale itself is fp16(absmax / qmax): fp32 division rounded once more
 // to fp16 equals the correctly rounded quotient for every fp16 absmax (a
 // quotient that is not exactly an fp16 midpoint lies at least 2^-12 / qmax
@@ -94,14 +96,32 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits, int qmax, uint
     return rs;
 }
 
+// The code plus 128 as a float (an exact integer in [128 - qmax, 128 + qmax]),
+// for the vector paths: the tie fix of code_of done in float.  At an exact
+// tie the residual e is +-s/2 and q0 + copysign(1/2, e) is exactly the
+// half-integer x/s, whose round-to-nearest-even is the even neighbour; off a
+// tie the adjustment is 0 and q0 is the code.
+__device__ __forceinline__ float code_plus_128(float x, const RowScale &rs)
+{
+    const float q0 = __builtin_rintf(x * rs.r);
+    const float e = __builtin_fmaf(-q0, rs.s, x);
+    const float adj = (__builtin_fabsf(e) == rs.hs) ? __builtin_copysignf(0.5f, e) : 0.0f;
+    const float q = __builtin_rintf(q0 + adj) + 128.0f;
+    return __builtin_fminf(__builtin_fmaxf(q, 128.0f - (float)rs.qmax), 128.0f + (float)rs.qmax);
+}
+
+// Four fp16 values (two dwords) -> their four int8 codes (byte i = value i):
+// each code + 128 is converted into its byte (v_cvt_pk_u8_f32, exact for
+// these integers) and the bias removed from all four at once (code + 128 xor
+// 0x80 is the code's two's complement byte).
 __device__ __forceinline__ uint32_t codes4(uint32_t w0, uint32_t w1, const RowScale &rs)
 {
-    const int c0 = code_of(half_bits_to_float(w0 & 0xFFFF), rs.s, rs.r, rs.hs, rs.qmax);
-    const int c1 = code_of(half_bits_to_float(w0 >> 16), rs.s, rs.r, rs.hs, rs.qmax);
-    const int c2 = code_of(half_bits_to_float(w1 & 0xFFFF), rs.s, rs.r, rs.hs, rs.qmax);
-    const int c3 = code_of(half_bits_to_float(w1 >> 16), rs.s, rs.r, rs.hs, rs.qmax);
-    return (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
-           ((uint32_t)(c2 & 0xFF) << 16) | ((uint32_t)(c3 & 0xFF) << 24);
+    uint32_t o = 0;
+    o = __builtin_amdgcn_cvt_pk_u8_f32(code_plus_128(half_bits_to_float(w0 & 0xFFFF), rs), 0, o);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(code_plus_128(half_bits_to_float(w0 >> 16), rs), 1, o);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(code_plus_128(half_bits_to_float(w1 & 0xFFFF), rs), 2, o);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(code_plus_128(half_bits_to_float(w1 >> 16), rs), 3, o);
+    return o ^ 0x80808080u;
 }
 
 // Vector path: cols % 8 == 0, so a row is whole 16-byte vectors of 8 fp16
