@@ -107,7 +107,7 @@ __device__ __forceinline__ float code_plus_128(float x, const RowScale &rs)
     const float e = __builtin_fmaf(-q0, rs.s, x);
     const float adj = (__builtin_fabsf(e) == rs.hs) ? __builtin_copysignf(0.5f, e) : 0.0f;
     const float q = __builtin_rintf(q0 + adj) + 128.0f;
-    return __builtin_fminf(__builtin_fmaxf(q, 128.0f - (float)rs.qmax), 128.0f + (float)rs.qmax);
+    return __builtin_amdgcn_fmed3f(q, 128.0f - (float)rs.qmax, 128.0f + (float)rs.qmax);
 }
 
 // Four fp16 values (two dwords) -> their four int8 codes (byte i = value i):
