@@ -759,6 +759,28 @@ def cpu_oracle_configs(W, A64, A1, B4v, A2, B2v, s4, s2, gpu_us):
     _, B11v, s11 = synth.w4a8_case(1, 11008, W.shape[1], seed=0)
     B11p = oracle.pack_int4(B11v)
     timed("gemm_w4a8_m1_n11008", lambda: oracle.gemm_wxa8_dequant(A1, B11p, s11, 4))
+    # single-thread times of the quantize and the M <= 64 workloads, in a
+    # child process (the thread count of the oracle's OpenMP is fixed at load)
+    import subprocess
+
+    code = (
+        "import sys, time, json, numpy as np; sys.path.insert(0, %r)\n"
+        "import oracle; from bit_mixed_precision_amd import synth\n"
+        "W, A64 = synth.bminf_case(M=64, rows=3 * 4096, cols=4096, seed=0)\n"
+        "A, B4v, s4 = synth.w4a8_case(1, 4096, 4096, seed=0)\n"
+        "B4p = oracle.pack_int4(B4v); r = {}\n"
+        "t = time.perf_counter(); q, s = oracle.quantize_rows(W); r['quantize_rows'] = time.perf_counter() - t\n"
+        "t = time.perf_counter(); oracle.gemm_wxa8_dequant(A64, q, s, 8); r['gemm_w8a8_m64'] = time.perf_counter() - t\n"
+        "t = time.perf_counter(); oracle.gemm_wxa8_dequant(A, B4p, s4, 4); r['gemm_w4a8_m1'] = time.perf_counter() - t\n"
+        "print(json.dumps(r))\n" % ROOT)
+    try:
+        res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                             env={**os.environ, "OMP_NUM_THREADS": "1"})
+        one = json.loads(res.stdout.strip().splitlines()[-1])
+        for k, v in one.items():
+            out[k]["oracle_ms_1thread"] = round(v * 1e3, 2)
+    except Exception as e:  # reported, not fatal: the all-cores times stand
+        out["single_thread_error"] = str(e)[:200]
     return out
 
 
