@@ -243,3 +243,36 @@ def test_error_paths(dev):
         bq.gemm(torch.zeros((5, 64), dtype=torch.int8, device=dev),
                 torch.zeros((4, 64), dtype=torch.int8, device=dev), 8, path="gemv")
     assert e.value.status == bq.BQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("N", [6143, 6144, 6145, 6200])
+def test_decode_gemv_rows_rule_boundary(dev, bits, N):
+    """M = 1 around the switch between one and two B rows per wavefront
+    (6144 rows per launch), K = 1024, compared in full."""
+    banner(f"gemm decode rows-rule boundary bits={bits} N={N}")
+    A, Bv, Bp, s = _make(bits, 1, N, 1024, seed=N + bits)
+    acc, C = _run(dev, bits, A, Bp, s, "gemv")
+    _check(acc, C, A, Bv, s, what=f"w{bits} gemv 1x{N}x1024")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_gemv_batched_rows_rule(dev, bits):
+    """Batched M = 1 GEMV where N x batch crosses the 6144-row switch
+    (3 x 2112 = 6336 rows: two rows per wavefront; 2 x 2112: one; 2112 keeps
+    every batch's scale and output 16-byte aligned)."""
+    import torch
+
+    from bit_mixed_precision_amd import bq
+
+    for batch in (2, 3):
+        banner(f"gemm decode batched rows rule bits={bits} batch={batch}")
+        A, Bv, Bp, s = _make(bits, 1, 2112 * batch, 512, seed=batch * 10 + bits)
+        Bb = to_dev(Bp.reshape(batch, 2112, -1), dev)
+        sb = to_dev(s.reshape(batch, 2112), dev)
+        C = bq.gemm_batched(to_dev(A, dev), Bb, bits, sb, path="gemv")
+        acc = bq.gemm_batched(to_dev(A, dev), Bb, bits, None, path="gemv")
+        torch.cuda.synchronize()
+        got_acc = acc.cpu().numpy().transpose(1, 0, 2).reshape(1, -1)
+        got_C = f16_bits(C).transpose(1, 0, 2).reshape(1, -1)
+        _check(got_acc, got_C, A, Bv, s, what=f"w{bits} batched gemv x{batch}")
