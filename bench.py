@@ -62,7 +62,7 @@ def parse():
 # Kernel sources of the tiled matrix-core GEMM; the committed HBM-traffic
 # summary is used only while their code (comments and blank space aside) and
 # the compiler flags are unchanged.
-TILED_SOURCES = ["gemm_tiled.hip", "unpack.h", "bq_internal.h", "nf4_table.h"]
+TILED_SOURCES = ["gemm_tiled.hip", "unpack.h", "bq_internal.h", "nf4_table.h", "erfc_fit.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a8_m4096_hbm_traffic.txt")
 
 

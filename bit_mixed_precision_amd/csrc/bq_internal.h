@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "erfc_fit.h"
+
 namespace bq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -32,6 +34,25 @@ hipError_t launch_quantize_pack(const uint16_t *x, int64_t rows, int64_t cols, i
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 
+// erfc in fp32 for the GELU epilogue: exp(-x^2) * P(t), t = 1 / (1 + 0.4|x|),
+// with P the degree-8 fit of exp(x^2) erfc(x) on [0, 4.5] from
+// gen_erfc_fit.py (relative error about 6e-9 in double; with the fp32
+// arithmetic here about 2e-6, far below half an fp16 ulp), erfc(-x) =
+// 2 - erfc(x); |x| is clamped to 4.5, past which GELU's value is far below
+// half the smallest fp16 subnormal.  About 15 VALU operations.
+__device__ __forceinline__ float erfc_fit(float x)
+{
+    const float ax = fminf(fabsf(x), kErfcFitXmax);
+    const float t = __builtin_amdgcn_rcpf(1.0f + kErfcFitP * ax);
+    float p = kErfcFitC[kErfcFitDeg];
+#pragma unroll
+    for (int k = kErfcFitDeg - 1; k >= 0; --k)
+        p = __builtin_fmaf(p, t, kErfcFitC[k]);
+    const float e = __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
+    const float E = e * p;
+    return x >= 0.0f ? E : 2.0f - E;
+}
+
 // Activation applied to the dequantized fp32 value before the fp16
 // conversion: 0 identity, 1 ReLU, 2 GELU v * Phi(v) with the standard normal
 // CDF Phi(v) = erfc(-v / sqrt(2)) / 2 (no cancellation for negative v).
@@ -40,7 +61,7 @@ __device__ __forceinline__ float apply_act(float v, int act)
     if (act == 1)
         return fmaxf(v, 0.0f);
     if (act == 2)
-        return 0.5f * v * erfcf(-v * 0.70710678118654752f);
+        return 0.5f * v * erfc_fit(-v * 0.70710678118654752f);
     return v;
 }
 

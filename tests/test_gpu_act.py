@@ -69,3 +69,30 @@ def test_linear_gelu_flow(dev):
     qx, sx = oracle.quantize_rows(X)
     ref = oracle.dequant_act(oracle.gemm_i32(qx, Bv), ws, sx, "gelu")
     assert_f16_within_1ulp(f16_bits(C), ref, "linear gelu")
+
+
+@pytest.mark.parametrize("path", ["tiled", "stream", "gemv"])
+def test_gelu_dense_sweep(dev, path):
+    """GELU over a dense grid of dequantized values: acc[m, n] = a_m for
+    a = -127..127 (A[m, 0] = a_m, B[n, 0] = 1, everything else 0) and 256
+    weight scales from 2^-8 to 2^-3, so v = a_m * s_n covers [-16, 16] with
+    steps down to 2^-8; fp16 outputs within 1 ulp of the exact GELU."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    banner(f"gelu dense sweep path={path}")
+    a = np.arange(-127, 128, dtype=np.int8)
+    if path == "stream":
+        a = a[::4][:64]
+    elif path == "gemv":
+        a = np.array([-127, -3, 5, 126], dtype=np.int8)
+    M, N, K = len(a), 256, 64
+    A = np.zeros((M, K), np.int8)
+    A[:, 0] = a
+    Bv = np.zeros((N, K), np.int8)
+    Bv[:, 0] = 1
+    ws = np.exp2(np.linspace(-8.0, -3.0, N)).astype(np.float16)
+    C = bq.gemm_act(to_dev(A, dev), to_dev(Bv, dev), 8, to_dev(ws, dev), None, act="gelu", path=path)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_act(oracle.gemm_i32(A, Bv), ws, None, "gelu")
+    assert_f16_within_1ulp(f16_bits(C), ref, f"gelu sweep {path}")
