@@ -161,6 +161,22 @@ def test_w4a8_prefill_sweep(dev, M):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 1024), (4100, 4130, 576)])
+def test_largest_tile_configuration(dev, bits, M, N, K):
+    """The 256 x 256 tile configuration (chosen once there are 256 such tiles)
+    for every weight width, int32 and fp16 outputs, without and with M, N and
+    K tails (K = 576 ends in half a 128-k stage); sampled rows and columns,
+    the ragged last tile row and column included."""
+    banner(f"gemm largest tiles w{bits} M={M} N={N} K={K}")
+    A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
+    acc, C = _run(dev, bits, A, Bp, s, "auto")
+    g = np.random.default_rng(M + N + bits)
+    rows = np.unique(np.concatenate([g.choice(M, 64, replace=False), np.arange(M - 8, M), [0]]))
+    cols = np.unique(np.concatenate([g.choice(N, 768, replace=False), np.arange(N - 40, N), [0]]))
+    _check(acc, C, A, Bv, s, rows=rows, cols=cols, what=f"w{bits} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
 @pytest.mark.parametrize("path", ["gemv", "stream", "tiled"])
 def test_k_zero_and_empty(dev, bits, path):
     from bit_mixed_precision_amd import bq
