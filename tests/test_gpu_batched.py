@@ -58,6 +58,33 @@ def test_batched_broadcast_parity(dev, bits, path, shape):
     assert_f16_within_1ulp(f16_bits(C2), oracle.gemm_batched(A, Bp, bits, ws, xs), f"batched2 w{bits} {path}")
 
 
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_batched_largest_tile_configuration(dev, bits):
+    """Two weights of 4104 x 128 behind one 4100 x 128 activation: 289 tiles of
+    256 x 256 per weight, so the batch runs the largest tile configuration with
+    M and N tails (N a multiple of 8, so that each weight's scale row starts
+    16-byte aligned); int32, one- and two-scale outputs on sampled rows and
+    columns of both weights, the ragged last tile row and column included."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    batch, M, N, K = 2, 4100, 4104, 128
+    banner(f"batched largest tiles bits={bits} batch={batch} M={M} N={N} K={K}")
+    A, Bp, ws, xs = _case(bits, batch, M, N, K, seed=41 + bits)
+    Ad, Bd, wsd, xsd = to_dev(A, dev), to_dev(Bp, dev), to_dev(ws, dev), to_dev(xs, dev)
+    acc = bq.gemm_batched(Ad, Bd, bits).cpu().numpy()
+    C1 = f16_bits(bq.gemm_batched(Ad, Bd, bits, wsd))
+    C2 = f16_bits(bq.gemm_batched(Ad, Bd, bits, wsd, xsd))
+    g = np.random.default_rng(bits)
+    rows = np.unique(np.concatenate([g.choice(M, 48, replace=False), np.arange(M - 8, M), [0]]))
+    cols = np.unique(np.concatenate([g.choice(N, 512, replace=False), np.arange(N - 40, N), [0]]))
+    A_s, B_s, ws_s = np.ascontiguousarray(A[rows]), np.ascontiguousarray(Bp[:, cols]), np.ascontiguousarray(ws[:, cols])
+    sel = np.ix_(np.arange(batch), rows, cols)
+    assert np.array_equal(acc[sel], oracle.gemm_batched(A_s, B_s, bits))
+    assert_f16_within_1ulp(C1[sel], oracle.gemm_batched(A_s, B_s, bits, ws_s), f"batched large w{bits}")
+    assert_f16_within_1ulp(C2[sel], oracle.gemm_batched(A_s, B_s, bits, ws_s, xs[rows]), f"batched2 large w{bits}")
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 def test_batched_per_batch_activations(dev, bits):
     from bit_mixed_precision_amd import bq
