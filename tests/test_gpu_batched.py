@@ -145,5 +145,16 @@ def test_batched_errors(dev):
                              2, 4, 8, 64, 0, S) == bq.BQ_ERR_ALIGN
     assert L.bq_gemm_batched(A.data_ptr(), 0, B.data_ptr(), 512, 8, None, 0, None, C.data_ptr(), 32,
                              65536, 4, 8, 64, 0, S) == bq.BQ_ERR_SHAPE
+    # fp16 outputs: a weight-scale stride or an output stride that is not a
+    # multiple of 8 elements leaves the next batch's row misaligned
+    W = torch.ones((2, 16), dtype=torch.float16, device=dev)
+    H = torch.zeros((2, 40), dtype=torch.float16, device=dev)
+    assert L.bq_gemm_batched(A.data_ptr(), 0, B.data_ptr(), 512, 8, W.data_ptr(), 4, None, H.data_ptr(), 40,
+                             2, 4, 8, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm_batched(A.data_ptr(), 0, B.data_ptr(), 512, 8, W.data_ptr(), 8, None, H.data_ptr(), 36,
+                             2, 4, 8, 64, 0, S) == bq.BQ_ERR_ALIGN
+    assert L.bq_gemm_batched(A.data_ptr(), 0, B.data_ptr(), 512, 8, W.data_ptr(), 8, None, H.data_ptr(), 40,
+                             2, 4, 8, 64, 0, S) == bq.BQ_OK
+    torch.cuda.synchronize()
     # batch 0 is a no-op
     assert L.bq_gemm_batched(None, 0, None, 0, 8, None, 0, None, None, 0, 0, 4, 8, 64, 0, S) == bq.BQ_OK
