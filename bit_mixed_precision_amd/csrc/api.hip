@@ -68,7 +68,7 @@ int validate_gemm(const int8_t *A, const void *B, int bits, const void *scale, v
         return BQ_ERR_ARG;
     if (M < 0 || N < 0 || K < 0 || K > BQ_MAX_K || (K % 64) != 0)
         return BQ_ERR_SHAPE;
-    if (M > INT32_MAX || N > INT32_MAX)
+    if (M > BQ_MAX_DIM || N > BQ_MAX_DIM || M * N > BQ_MAX_OUT)
         return BQ_ERR_SHAPE;
     if (path == BQ_PATH_STREAM && M > kStreamMaxM)
         return BQ_ERR_SHAPE;
@@ -289,7 +289,8 @@ int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f1
 int bq_gemm_nf4_a16(const void *A_f16, const uint8_t *B, const void *scale_f16, const void *zero_f16,
                     void *C_f16, int64_t M, int64_t N, int64_t K, void *stream)
 {
-    if (M < 0 || N < 0 || K < 0 || K > BQ_MAX_K || (K % 64) != 0 || M > INT32_MAX || N > INT32_MAX)
+    if (M < 0 || N < 0 || K < 0 || K > BQ_MAX_K || (K % 64) != 0 || M > BQ_MAX_DIM || N > BQ_MAX_DIM ||
+        M * N > BQ_MAX_OUT)
         return BQ_ERR_SHAPE;
     if (M == 0 || N == 0)
         return BQ_OK;

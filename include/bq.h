@@ -78,6 +78,13 @@ enum bq_status {
  * limit leaves a factor of two of headroom. */
 #define BQ_MAX_K 65536
 
+/* Largest M and N accepted by the GEMMs, and the largest output M * N.  The
+ * launchers size their grids in 32-bit arithmetic and a launch holds at most
+ * 2^31 - 1 workgroups; these bounds keep both exact.  An output at the limit
+ * holds 2^42 elements (8 TiB in fp16), more than one device's memory. */
+#define BQ_MAX_DIM (1LL << 30)
+#define BQ_MAX_OUT (1LL << 42)
+
 /* GEMM path selection for bq_gemm (the named GEMM calls use BQ_PATH_AUTO). */
 enum bq_path {
     BQ_PATH_AUTO = 0,   /* choose by M (see bq_gemm_select_path)              */
@@ -176,8 +183,9 @@ int bq_pack_int2(const int8_t *v, int64_t n, int64_t k, uint8_t *out, void *stre
  *             w2: uint8 [N, K/4] (bq_pack_int2 layout)
  *   scale_f16 [N]               fp16
  *   C_f16     [M, N]            fp16 output, row-major
- * M, N >= 0; 0 <= K <= BQ_MAX_K and K % 64 == 0 (an implementation limit;
- * pad K with zero columns of A otherwise).  K == 0 writes zeros.
+ * 0 <= M, N <= BQ_MAX_DIM, M * N <= BQ_MAX_OUT; 0 <= K <= BQ_MAX_K and
+ * K % 64 == 0 (an implementation limit; pad K with zero columns of A
+ * otherwise).  K == 0 writes zeros.
  */
 int bq_gemm_w8a8_dequant(const int8_t *A, const int8_t *B, const void *scale_f16,
                          void *C_f16, int64_t M, int64_t N, int64_t K, void *stream);
@@ -307,7 +315,8 @@ int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f1
  *              the high nibble (codes 0..15)
  *   scale_f16  [N] fp16 (required); zero_f16 [N] fp16 or NULL
  *   C_f16      [M, N] fp16
- * M, N >= 0; 0 <= K <= BQ_MAX_K, K % 64 == 0 (BQ_ERR_SHAPE); pointers
+ * 0 <= M, N <= BQ_MAX_DIM, M * N <= BQ_MAX_OUT; 0 <= K <= BQ_MAX_K,
+ * K % 64 == 0 (BQ_ERR_SHAPE); pointers
  * 16-byte aligned (BQ_ERR_ALIGN); NULL where required (BQ_ERR_NULL).  M <= 4
  * runs a decode GEMV (dot products on the vector ALUs, a stream over B);
  * larger M the tiled matrix-core kernel (with the K split of the

@@ -73,8 +73,12 @@ def test_gemm_validation(bq):
     assert L.bq_gemm(P16, P16b, 4, P16c, P16d, 4, 4, 64, 7, S) == bq.BQ_ERR_ARG
     # shapes
     for M, N, K in [(-1, 4, 64), (4, -1, 64), (4, 4, -64), (4, 4, 32), (4, 4, 100),
-                    (4, 4, 65536 + 64), (2**31, 4, 64)]:
+                    (4, 4, 65536 + 64), (2**31, 4, 64), (2**30 + 1, 4, 64), (4, 2**30 + 1, 64),
+                    (2**30, 2**12 + 1, 64), (2**21, 2**21 + 1, 64)]:
         assert L.bq_gemm(P16, P16b, 8, P16c, P16d, M, N, K, 0, S) == bq.BQ_ERR_SHAPE, (M, N, K)
+    # the dimension and output limits are inclusive: the next check (NULL) decides
+    assert L.bq_gemm(NULL, P16b, 8, P16c, P16d, 2**30, 4, 64, 0, S) == bq.BQ_ERR_NULL
+    assert L.bq_gemm(NULL, P16b, 8, P16c, P16d, 2**21, 2**21, 64, 0, S) == bq.BQ_ERR_NULL
     # the streaming kernel only takes M <= 64
     assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 65, 4, 64, 1, S) == bq.BQ_ERR_SHAPE
     # the GEMV path only takes M <= 4
@@ -170,6 +174,9 @@ def test_nf4_validation(bq):
     assert f(P16, P16b, P16c, NULL, P16d, 4, 4, 96, S) == bq.BQ_ERR_SHAPE   # K % 64
     assert f(P16, P16b, P16c, NULL, P16d, -1, 4, 64, S) == bq.BQ_ERR_SHAPE
     assert f(P16, P16b, P16c, NULL, P16d, 4, 4, 65536 + 64, S) == bq.BQ_ERR_SHAPE
+    assert f(P16, P16b, P16c, NULL, P16d, 2**30 + 1, 4, 64, S) == bq.BQ_ERR_SHAPE
+    assert f(P16, P16b, P16c, NULL, P16d, 2**21, 2**21 + 1, 64, S) == bq.BQ_ERR_SHAPE
+    assert f(NULL, P16b, P16c, NULL, P16d, 2**21, 2**21, 64, S) == bq.BQ_ERR_NULL
     assert f(P16, P16b, NULL, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_NULL    # scale required
     assert f(NULL, P16b, P16c, NULL, P16d, 4, 4, 64, S) == bq.BQ_ERR_NULL
     assert f(P16, P16b, P16c, PODD, P16d, 4, 4, 64, S) == bq.BQ_ERR_ALIGN   # zero point
