@@ -44,7 +44,10 @@ SIGNATURES = {
     "bq_quantize_pack": [_P, _I64, _I64, _I, _P, _P, _P],
     "bq_gemm_select_path": [_I64, _I64, _I64, _I],
     "bq_gemm_nf4_a16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P],
+    "bq_gemm_splitk_workspace_bytes": [_I64, _I64, _I64, _I],
+    "bq_gemm_splitk": [_P, _P, _I, _P, _P, _I64, _I64, _I64, _P, _I64, _P],
 }
+_RESTYPES = {"bq_status_string": ctypes.c_char_p, "bq_gemm_splitk_workspace_bytes": ctypes.c_int64}
 
 
 class BQError(RuntimeError):
@@ -68,7 +71,7 @@ def lib() -> ctypes.CDLL:
         for name, args in SIGNATURES.items():
             fn = getattr(handle, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "bq_status_string" else ctypes.c_int
+            fn.restype = _RESTYPES.get(name, ctypes.c_int)
         _lib = handle
     return _lib
 
@@ -241,6 +244,31 @@ def gemm(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tens
     """
     M, N, K, dev, out = _gemm_args(A, B, bits, scale, out)
     _call("bq_gemm", dev, _ptr(A), _ptr(B), bits, _ptr(scale), _ptr(out), M, N, K, _PATHS[path])
+    return out
+
+
+def gemm_splitk_workspace_bytes(M: int, N: int, K: int, bits: int) -> int:
+    """Device workspace bytes gemm_splitk uses to split K for this shape (0:
+    it would not split)."""
+    n = lib().bq_gemm_splitk_workspace_bytes(M, N, K, bits)
+    if n < 0:
+        raise BQError(-n, "bq_gemm_splitk_workspace_bytes")
+    return n
+
+
+def gemm_splitk(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tensor],
+                workspace: Optional[torch.Tensor], out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm on the tiled path with K split over workgroups when the output
+    has few tiles, using the caller's workspace (a uint8 device tensor whose
+    first 4096 bytes are zero before the first call, e.g. torch.zeros of
+    gemm_splitk_workspace_bytes(M, N, K, bits) bytes; None: no split)."""
+    M, N, K, dev, out = _gemm_args(A, B, bits, scale, out)
+    nbytes = 0
+    if workspace is not None:
+        _check_tensor(workspace, "workspace", torch.uint8, None, dev)
+        nbytes = workspace.numel()
+    _call("bq_gemm_splitk", dev, _ptr(A), _ptr(B), bits, _ptr(scale), _ptr(out), M, N, K, _ptr(workspace),
+          nbytes)
     return out
 
 

@@ -39,22 +39,30 @@ int check_device()
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? BQ_OK : BQ_ERR_HIP; }
+// A launcher's grid check (kGridTooLarge) is a shape error; nothing was
+// launched.  Any other failure is the runtime's.
+int launch_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return BQ_OK;
+    return e == bq::kGridTooLarge ? BQ_ERR_SHAPE : BQ_ERR_HIP;
+}
 
 // Largest M handled by the streaming kernel (when asked for), and the largest
 // M for which automatic dispatch takes it.  Below the MI355X ridge point
-// (about 625 int8 ops per byte) the GEMM is bound by moving B; the streaming
-// kernel reads A from the caches once per matrix instruction, so its cost
-// grows with M, while the tiled kernel stages A through LDS.  Measured on
-// MI355X (W4A8, N = K = 4096): 5.8 / 9.0 / 13.5 us at M = 16 / 32 / 64 for
-// the streaming kernel against 11.2 / - / 12.1 us tiled; W8A8 at M = 64,
-// N = 12288: 28.6 us streaming, 15 us tiled.
-constexpr int64_t kStreamMaxM = 64;
-constexpr int64_t kStreamAutoMaxM = 32;
+// (about 625 int8 operations per byte) the GEMM is bound by moving its
+// operands; the streaming kernel loads A and B straight into matrix-core
+// registers with K split over a workgroup's wavefronts, so its cost is the
+// per-CU operand traffic (TM + TN bits/8) K of its tiles, while the tiled
+// kernel stages tiles through LDS and reuses them across a larger tile.
+// Measured (kernel trace, N = K = 4096): W4A8 M = 64 6.1 us streaming
+// against 10.0 tiled, M = 128 7.8 against 10.4, M = 256 11.2 against 11.0;
+// W8A8 M = 256 12.6 against 12.7; W2A8 M = 256 11.0 against 13.0.
+constexpr int64_t kStreamMaxM = 256;
+constexpr int64_t kStreamAutoMaxM = 128;
+constexpr int64_t kStreamAutoMaxM2 = 256;  // int2 weights
 // The dot-product GEMV accepts M <= 4 (each B byte feeds at most M
-// multiply-adds); automatic dispatch uses it up to M = 2, where it is faster
-// than the streaming matrix-core kernel (measured on MI355X at N = K = 4096:
-// 4.0 vs 5.2 us at M = 1, 4.6 vs 5.2 us at M = 2, 5.6 vs 5.3 us at M = 3).
+// multiply-adds); automatic dispatch uses it up to M = 2.
 constexpr int64_t kGemvMaxM = 4;
 constexpr int64_t kGemvAutoMaxM = 2;
 
@@ -190,15 +198,15 @@ int bq_gemm_select_path(int64_t M, int64_t N, int64_t K, int bits)
 {
     (void)N;
     (void)K;
-    (void)bits;
     if (M <= kGemvAutoMaxM)
         return BQ_PATH_GEMV;
-    return M <= kStreamAutoMaxM ? BQ_PATH_STREAM : BQ_PATH_TILED;
+    return M <= (bits == 2 ? kStreamAutoMaxM2 : kStreamAutoMaxM) ? BQ_PATH_STREAM : BQ_PATH_TILED;
 }
 
 static int gemm_common(const int8_t *A, const void *B, int bits, const void *scale_f16,
                        const void *xscale_f16, int act, void *C, int64_t M, int64_t N, int64_t K,
-                       int path, void *stream, int batch = 1, const bq::BatchStrides &bs = {})
+                       int path, void *stream, int batch = 1, const bq::BatchStrides &bs = {},
+                       void *ws = nullptr, int64_t wsBytes = 0)
 {
     int st = validate_gemm(A, B, bits, scale_f16, C, M, N, K, path);
     if (st != BQ_OK || M == 0 || N == 0)
@@ -216,13 +224,37 @@ static int gemm_common(const int8_t *A, const void *B, int bits, const void *sca
         return launch_status(bq::launch_gemv(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s));
     if (path == BQ_PATH_STREAM)
         return launch_status(bq::launch_gemm_stream(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s));
-    return launch_status(bq::launch_gemm_tiled(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s));
+    return launch_status(
+        bq::launch_gemm_tiled(A, Bb, bits, sc, xs, act, C, (int)M, (int)N, (int)K, batch, bs, s, ws, wsBytes));
 }
 
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C,
             int64_t M, int64_t N, int64_t K, int path, void *stream)
 {
     return gemm_common(A, B, bits, scale_f16, nullptr, 0, C, M, N, K, path, stream);
+}
+
+int64_t bq_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits)
+{
+    if (bits != 8 && bits != 4 && bits != 2)
+        return -BQ_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0 || K > BQ_MAX_K || (K % 64) != 0 || M > BQ_MAX_DIM || N > BQ_MAX_DIM ||
+        M * N > BQ_MAX_OUT)
+        return -BQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return 0;
+    return bq::gemm_splitk_workspace_bytes((int)M, (int)N, (int)K, bits);
+}
+
+int bq_gemm_splitk(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C, int64_t M,
+                   int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+        return workspace_bytes < 0 ? BQ_ERR_SHAPE : BQ_ERR_NULL;
+    if (workspace && !aligned16(workspace))
+        return BQ_ERR_ALIGN;
+    return gemm_common(A, B, bits, scale_f16, nullptr, 0, C, M, N, K, BQ_PATH_TILED, stream, 1, {},
+                       workspace_bytes > 0 ? workspace : nullptr, workspace_bytes);
 }
 
 // Largest batch of bq_gemm_batched (the grid's y dimension).

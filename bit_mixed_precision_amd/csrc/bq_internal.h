@@ -21,6 +21,13 @@ __device__ __forceinline__ uint4 load_nt16(const void *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A dispatch counts work-items, not workgroups, per grid dimension, and the
+// count must stay below 2^32.  Launchers check their grid with grid_fits and
+// return kGridTooLarge (reported as a shape error by the C ABI) instead of
+// launching when it does not.
+constexpr hipError_t kGridTooLarge = hipErrorInvalidConfiguration;
+inline bool grid_fits(int64_t workgroups, int threads) { return workgroups * threads < (1LL << 32); }
+
 // Kernel launchers.  Arguments have been validated by the C ABI layer:
 // sizes are non-negative and within limits, pointers non-null and aligned.
 // Each returns the status of the launch (hipGetLastError after it).
@@ -80,14 +87,21 @@ struct BatchStrides {
 // Decode GEMV on the dot-product ALUs, M <= 4.
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
                        const uint16_t *xscale, int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
-// Streaming skinny-M GEMM, M <= 64.
+// Streaming matrix-core GEMM (operands straight into registers, K split over
+// the wavefronts of a workgroup), M <= 256.
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
                               const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                               int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
-// LDS-tiled matrix-core GEMM, any M.
+// LDS-tiled matrix-core GEMM, any M.  With a workspace (ws, wsBytes) of at
+// least gemm_splitk_workspace_bytes(M, N, K, bits) bytes whose first 4 KiB
+// are zero, a shape with few output tiles splits K over workgroups; without
+// one (ws == nullptr) K is never split.
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
                              const uint16_t *scale, const uint16_t *xscale, int act, void *C,
-                             int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
+                             int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
+                             void *ws = nullptr, int64_t wsBytes = 0);
+// Workspace bytes the tiled GEMM uses to split K for this shape (0: no split).
+int64_t gemm_splitk_workspace_bytes(int M, int N, int K, int bits);
 // W4A16 GEMM with NF4 weight codes on the tiled kernel: A fp16 [M, K], B
 // codes [N, K/2], per-row scale and zero point (zero may be NULL), C fp16.
 hipError_t launch_gemm_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero,

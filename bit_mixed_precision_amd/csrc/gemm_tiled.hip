@@ -38,8 +38,9 @@
 //    stage ahead.
 //  * Epilogue: fp16(acc * scale) rows are staged through LDS and written
 //    with 16-byte coalesced stores.
-//  * With few output tiles, K is split over several workgroups per tile;
-//    the last to finish adds the others' partial sums (SplitK below).
+//  * With few output tiles and a workspace from the caller, K is split over
+//    several workgroups per tile; the last to finish adds the others'
+//    partial sums (SplitK below).
 //  * An NF4 mode (fp16 activations, 4-bit NormalFloat weight codes) reuses
 //    the same ring and loops with fp16 matrix-core operands (see the kernel).
 // Workgroups are mapped so that the tiles one XCD runs (blockIdx modulo 8
@@ -48,22 +49,17 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
-#include <mutex>
-#include <vector>
-
 #include "bq_internal.h"
+#include "lds_dma.h"
 #include "nf4_table.h"
 #include "unpack.h"
 
 namespace bq {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 constexpr int kBK = 128;  // unpacked k per stage
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
-constexpr uint32_t kOOB = 0x80000000u;  // buffer offset that is always out of range
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x002;
@@ -72,7 +68,6 @@ constexpr int kSchedDsRead = 0x100;
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-typedef int v4si __attribute__((ext_vector_type(4)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -139,56 +134,6 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 &p, int i)
     return i == 0 ? p.x : i == 1 ? p.y : i == 2 ? p.z : p.w;
 }
 
-// Raw buffer resource (gfx9 layout): base address, stride 0, byte range,
-// default format word.  Offsets at or past `bytes` read as zero.
-__device__ __forceinline__ v4si make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)base;
-    return (v4si){(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), (int)bytes, 0x00020000};
-}
-
-// 16-byte buffer load written straight to LDS: lane i stores its 16 bytes at
-// LDS address lds_addr + 16 i.  Issued as inline assembly so the compiler's
-// wait-count pass does not order every later LDS read behind it; the kernel
-// waits for these loads explicitly (wait_vmcnt) before the barrier that
-// publishes a stage.
-__device__ __forceinline__ void dma16(v4si rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff)
-{
-    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));
-}
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-
-// s_waitcnt with only the LDS / scalar-memory counter limited (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_lgkmcnt()
-{
-    static_assert(N >= 0 && N < 16, "lgkmcnt range");
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
-}
-
-// wait_vmcnt<F * c>() for a wave-uniform c in [0, C] (the counter limit must
-// be an immediate, so one branch per value).
-template <int F, int C>
-__device__ __forceinline__ void wait_vmcnt_rt(int c)
-{
-    if constexpr (C > 0) {
-        if (c == C) {
-            wait_vmcnt<F * C>();
-            return;
-        }
-        wait_vmcnt_rt<F, C - 1>(c);
-    } else {
-        wait_vmcnt<0>();
-    }
-}
-
 // K split of each output tile over `parts` workgroups: workgroup q of a tile
 // runs the 128-k stages [q stepsPer, (q+1) stepsPer) and stores its int32
 // partial sums; the last of the tile's workgroups to arrive (a per-tile
@@ -198,7 +143,7 @@ struct SplitK {
     int parts = 1;           // workgroups per output tile
     int stepsPer = 0;        // 128-k stages per workgroup
     int *ctr = nullptr;      // per-tile arrival counters, zero between launches
-    int4 *part = nullptr;    // partial sums: [tile][part][8-byte piece][thread]
+    int4 *part = nullptr;    // partial sums: [tile][part][16-byte piece][thread]
 };
 
 // WGM: wavefronts along M (2, or 1 for a 1 x WAVES grid whose wave tiles
@@ -701,59 +646,63 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     wait_vmcnt<0>();
 
     if constexpr (SPLIT) {
-        // Exchange of the partial sums, coherent across the XCDs without
-        // cache-wide write-back or invalidation: the partial sums are stored
-        // and loaded as agent-scope relaxed atomics (8 bytes at a time, lane-
-        // major, coalesced), which the compiler issues with the device-scope
-        // cache policy (written through to, and read from, the level shared
-        // by all XCDs), piece q of every lane next to piece q of the next lane.
-        // Every workgroup stores its sums and waits until the
-        // stores have completed before the barrier after which one thread
-        // counts the arrival; the last of the tile's workgroups then loads
-        // the others' sums and adds them to its own.
-        constexpr int kQ = T::kFM * T::kFN * 8;  // 8-byte pieces per lane
+        // Exchange of the partial sums through the caller's workspace, ordered
+        // by the AMDGPU memory model at agent scope (the XCDs' L2 caches are
+        // not coherent with each other): every workgroup stores its sums
+        // (lane-major, coalesced 16-byte stores), and each wavefront then
+        // executes an agent-scope release fence (buffer_wbl2 sc1 and
+        // s_waitcnt vmcnt(0): its stores are written back from this XCD's L2
+        // and complete) before the barrier after which one thread counts the
+        // arrival with an agent-scope atomic add.  The last workgroup of the
+        // tile to arrive executes an agent-scope acquire fence in every
+        // wavefront (buffer_inv sc1: later loads miss this XCD's L2) after the
+        // barrier that publishes the count, then loads the other parts' sums
+        // and adds them to its own.  This is the fence - barrier - atomic
+        // pattern of a grid-wide reduction, with the release half paid by every
+        // workgroup and the acquire half only by the last.
+        constexpr int kQ = T::kFM * T::kFN * 4;  // 16-byte pieces per lane
         const int64_t tile0 = (int64_t)t * sk.parts * kQ * kThreads + tid;
-        long long *mine = (long long *)sk.part + tile0 + (int64_t)split * kQ * kThreads;
+        int4 *mine = sk.part + tile0 + (int64_t)split * kQ * kThreads;
 #pragma unroll
         for (int i = 0; i < T::kFM; ++i)
 #pragma unroll
             for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint64_t v = (uint64_t)bits32(acc[i][j][2 * q]) | ((uint64_t)bits32(acc[i][j][2 * q + 1]) << 32);
-                    __hip_atomic_store(mine + ((i * T::kFN + j) * 8 + q) * kThreads, (long long)v,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-        wait_vmcnt<0>();
+                for (int q = 0; q < 4; ++q)
+                    mine[((i * T::kFN + j) * 4 + q) * kThreads] =
+                        make_int4((int)bits32(acc[i][j][4 * q]), (int)bits32(acc[i][j][4 * q + 1]),
+                                  (int)bits32(acc[i][j][4 * q + 2]), (int)bits32(acc[i][j][4 * q + 3]));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
         __shared__ int lastArrival;
         if (tid == 0) {
-            const int arrived = atomicAdd(sk.ctr + t, 1) + 1;
+            const int arrived = __hip_atomic_fetch_add(sk.ctr + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
             lastArrival = arrived == sk.parts;
-            if (arrived == sk.parts)
-                atomicExch(sk.ctr + t, 0);  // ready for the next launch
+            if (arrived == sk.parts)  // ready for the next launch
+                __hip_atomic_store(sk.ctr + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (!lastArrival)
             return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         for (int p = 0; p < sk.parts; ++p) {
             if (p == split)
                 continue;
-            const long long *other = (const long long *)sk.part + tile0 + (int64_t)p * kQ * kThreads;
+            const int4 *other = sk.part + tile0 + (int64_t)p * kQ * kThreads;
 #pragma unroll
             for (int i = 0; i < T::kFM; ++i)
 #pragma unroll
                 for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const uint64_t v = (uint64_t)__hip_atomic_load(other + ((i * T::kFN + j) * 8 + q) * kThreads,
-                                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if constexpr (NF4) {
-                            acc[i][j][2 * q] += __uint_as_float((uint32_t)v);
-                            acc[i][j][2 * q + 1] += __uint_as_float((uint32_t)(v >> 32));
-                        } else {
-                            acc[i][j][2 * q] += (int)(uint32_t)v;
-                            acc[i][j][2 * q + 1] += (int)(uint32_t)(v >> 32);
+                    for (int q = 0; q < 4; ++q) {
+                        const int4 v = other[((i * T::kFN + j) * 4 + q) * kThreads];
+                        const int w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (NF4)
+                                acc[i][j][4 * q + e] += __uint_as_float((uint32_t)w[e]);
+                            else
+                                acc[i][j][4 * q + e] += w[e];
                         }
                     }
         }
@@ -869,12 +818,15 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
                     int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
                     const SplitK &sk = {})
 {
-    const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tilesM * tilesN * (SPLIT ? sk.parts : 1)), (unsigned)batch);
+    const int64_t tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
+    const int64_t wgs = tilesM * tilesN * (SPLIT ? sk.parts : 1);
+    if (!grid_fits(wgs, 64 * WAVES))
+        return kGridTooLarge;
+    const dim3 grid((unsigned)wgs, (unsigned)batch);
     const bool tail = (K % kBK) != 0;
 #define BQ_TILED_LAUNCH(F16, TAIL, FUSED)                                                                   \
     gemm_tiled_kernel<BITS, BM, BN, STAGES, F16, TAIL, WAVES, FUSED, SPLIT, NF4, WGM><<<grid, 64 * WAVES, 0, s>>>( \
-        A, B, scale, xscale, act, C, M, N, K, tilesM, tilesN, bs, sk)
+        A, B, scale, xscale, act, C, M, N, K, (int)tilesM, (int)tilesN, bs, sk)
     if constexpr (NF4) {
         // the row width of A is a whole number of 128-byte stages (K % 64 == 0)
         BQ_TILED_LAUNCH(true, false, false);
@@ -917,61 +869,37 @@ hipError_t launch_t(const int8_t *A, const uint8_t *B, const uint16_t *scale, co
 //    (M = 64: 11.0 -> 10.0 us; M = 128: 11.1 -> 10.4 us, W2A8 14.4 -> 11.9 us,
 //    W8A8 12.5 -> 11.0 us).
 
-// Split-K workspace of one (device, stream): the per-tile counters, then the
-// partial sums.  Allocated (and the counters zeroed on the stream) at the
-// first split launch on that stream, kept until the process ends; calls on
-// one stream are ordered, so they never share it concurrently.  A stream
-// under graph capture gets none (no allocation there): it runs unsplit.
+// K split over workgroups: only with a workspace from the caller (the
+// library allocates nothing).  The workspace holds the per-tile counters
+// (kCtrBytes, zero before the first use; every launch leaves them zero) and
+// then the partial sums of at most kSplitMaxWgs workgroups.
 constexpr int kSplitMaxTiles = 128;   // split only with this many tiles or fewer
 constexpr int kSplitMaxWgs = 256;     // tiles x parts
 constexpr int kSplitMaxParts = 8;
 constexpr int kSplitMinSteps = 4;     // 128-k stages per workgroup, at least
-constexpr size_t kCtrBytes = 4096;
-constexpr size_t kPartBytes = (size_t)kSplitMaxWgs * 256 * 16 * 4;  // 256 threads x 16 int32 each
+constexpr int64_t kCtrBytes = 4096;
+constexpr int64_t kPartBytesPerWg = 256 * 16 * 4;  // 256 threads x 16 int32 each
 
-struct Workspace {
-    int dev;
-    hipStream_t stream;
-    void *mem;
-};
-std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
-
-bool split_workspace(hipStream_t s, SplitK &sk)
+// Parts of the K split for a shape (1: no split).
+int split_parts(int M, int N, int K, int batch)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return false;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    void *mem = nullptr;
-    for (const Workspace &w : g_ws)
-        if (w.dev == dev && w.stream == s)
-            mem = w.mem;
-    if (!mem) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-            (void)hipGetLastError();
-            return false;
-        }
-        if (hipMalloc(&mem, kCtrBytes + kPartBytes) != hipSuccess) {
-            (void)hipGetLastError();
-            return false;
-        }
-        if (hipMemsetAsync(mem, 0, kCtrBytes, s) != hipSuccess) {
-            (void)hipGetLastError();
-            (void)hipFree(mem);
-            return false;
-        }
-        g_ws.push_back({dev, s, mem});
-    }
-    sk.ctr = (int *)mem;
-    sk.part = (int4 *)((char *)mem + kCtrBytes);
-    return true;
+    const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (batch != 1 || t64 > kSplitMaxTiles || t128 >= 192 || t64 >= 512)
+        return 1;
+    const int stepsAll = (K + kBK - 1) / kBK;
+    const int parts = min(kSplitMaxParts, min(kSplitMaxWgs / (int)t64, stepsAll / kSplitMinSteps));
+    if (parts < 2)
+        return 1;
+    // equal stage counts; the rounding never leaves a workgroup empty
+    const int per = (stepsAll + parts - 1) / parts;
+    return (stepsAll + per - 1) / per;
 }
 
 template <int BITS, bool NF4 = false>
 hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *xscale,
-                       int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
+                       int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
+                       void *ws, int64_t wsBytes)
 {
     // Three LDS stages fit in 160 KB except for 256x256 int8 (64 KB per stage).
     constexpr int kStages256 = BITS == 8 ? 2 : 3;
@@ -996,17 +924,15 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
     if (t64 >= 512)
         return launch_t<BITS, 64, 64, 4, kWaves64, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K,
                                                                            batch, bs, s);
-    if (batch == 1 && t64 <= kSplitMaxTiles) {
-        const int stepsAll = (K + kBK - 1) / kBK;
-        int parts = min(kSplitMaxParts, min(kSplitMaxWgs / (int)t64, stepsAll / kSplitMinSteps));
+    const int parts = ws ? split_parts(M, N, K, batch) : 1;
+    if (parts >= 2 && wsBytes >= kCtrBytes + t64 * parts * kPartBytesPerWg) {
         SplitK sk;
-        if (parts >= 2 && split_workspace(s, sk)) {
-            // equal stage counts; the rounding never leaves a workgroup empty
-            sk.stepsPer = (stepsAll + parts - 1) / parts;
-            sk.parts = (stepsAll + sk.stepsPer - 1) / sk.stepsPer;
-            return launch_t<BITS, 64, 64, 8, kWaves64, true, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K, 1,
-                                                                              bs, s, sk);
-        }
+        sk.parts = parts;
+        sk.stepsPer = ((K + kBK - 1) / kBK + parts - 1) / parts;
+        sk.ctr = (int *)ws;
+        sk.part = (int4 *)((char *)ws + kCtrBytes);
+        return launch_t<BITS, 64, 64, 8, kWaves64, true, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K, 1, bs,
+                                                                          s, sk);
     }
     return launch_t<BITS, 64, 64, 8, kWaves64, false, NF4, NF4 ? 1 : 2>(A, B, scale, xscale, act, C, M, N, K, batch,
                                                                          bs, s);
@@ -1014,25 +940,36 @@ hipError_t launch_bits(const int8_t *A, const uint8_t *B, const uint16_t *scale,
 
 }  // namespace
 
+int64_t gemm_splitk_workspace_bytes(int M, int N, int K, int bits)
+{
+    (void)bits;
+    const int parts = split_parts(M, N, K, 1);
+    if (parts < 2)
+        return 0;
+    const int64_t t64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+    return kCtrBytes + t64 * parts * kPartBytesPerWg;
+}
+
 hipError_t launch_gemm_nf4(const uint16_t *A, const uint8_t *B, const uint16_t *scale, const uint16_t *zero,
                            uint16_t *C, int M, int N, int K, hipStream_t s)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     // in the kernel's byte terms an A row is 2K bytes wide (see the kernel)
-    return launch_bits<2, true>((const int8_t *)A, B, scale, zero, 0, C, M, N, 2 * K, 1, {}, s);
+    return launch_bits<2, true>((const int8_t *)A, B, scale, zero, 0, C, M, N, 2 * K, 1, {}, s, nullptr, 0);
 }
 
 hipError_t launch_gemm_tiled(const int8_t *A, const uint8_t *B, int bits,
                              const uint16_t *scale, const uint16_t *xscale, int act, void *C,
-                             int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s)
+                             int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s,
+                             void *ws, int64_t wsBytes)
 {
     if (M == 0 || N == 0)
         return hipSuccess;
     switch (bits) {
-    case 8: return launch_bits<8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 4: return launch_bits<4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    default: return launch_bits<2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 8: return launch_bits<8>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s, ws, wsBytes);
+    case 4: return launch_bits<4>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s, ws, wsBytes);
+    default: return launch_bits<2>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s, ws, wsBytes);
     }
 }
 

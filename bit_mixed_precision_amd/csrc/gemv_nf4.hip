@@ -157,8 +157,10 @@ hipError_t launch_t(const uint16_t *A, const uint8_t *B, const uint16_t *scale, 
 {
     // kRows rows x 2 chunks of 16 bytes per lane per batch: one batch covers K = 4096
     constexpr int kU = 2;
-    const int waves = (N + kRows - 1) / kRows;
-    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+    const int64_t wgs = ((int64_t)N + kRows * kWaves - 1) / (kRows * kWaves);
+    if (!grid_fits(wgs, kThreads))
+        return kGridTooLarge;
+    const dim3 grid((unsigned)wgs);
     gemv_nf4_kernel<MR, kRows, kU><<<grid, kThreads, 0, s>>>(A, B, scale, zero, C, M, N, K);
     return hipGetLastError();
 }

@@ -289,6 +289,8 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int64_t cols, i
 {
     if (rows == 0)
         return hipSuccess;
+    if (!grid_fits(rows, kThreads))
+        return kGridTooLarge;
     const dim3 grid((unsigned)rows), block(kThreads);
     const int64_t nvec = cols / 8;
     const bool vec = (cols % 8 == 0) && cols > 0;
@@ -314,6 +316,8 @@ hipError_t launch_quantize_pack(const uint16_t *x, int64_t rows, int64_t cols, i
 {
     if (rows == 0)
         return hipSuccess;
+    if (!grid_fits(rows, kThreads))
+        return kGridTooLarge;
     const dim3 grid((unsigned)rows), block(kThreads);
     const int64_t nvec = cols / 8;
     const bool vec = (cols % 8 == 0) && cols > 0 && nvec <= 8 * kThreads;

@@ -39,20 +39,16 @@
  *    across the ABI.  A dimension of 0 (other than K) is a valid no-op.
  *  - The device must be gfx950 (BQ_ERR_DEVICE otherwise); the check is made
  *    once per device.
- *  - Library memory: a GEMM on the tiled kernel with few output tiles
- *    (64 x 64 tiles, at most 128 of them, K >= 1024, not batched) splits K
- *    over several workgroups per tile, which exchange int32 partial sums
- *    through a workspace of 4 MiB + 4 KiB.  The library allocates it with
- *    hipMalloc at the first such call on each (device, stream) and keeps it
- *    until the process ends; calls on one stream are ordered, so they never
- *    share it concurrently.  If the stream is being captured into a graph
- *    and has no workspace yet, or the allocation fails, the call runs with
- *    K unsplit (same results).  A graph captured with the split replays it
- *    on the workspace of the stream it was captured on: do not replay it
- *    concurrently with other work on that stream's GEMMs.
- *  - Thread safety: calls are reentrant; the shared state is a cached
- *    per-device property record, written once, and the workspace list
- *    above, guarded by a mutex.
+ *  - Library memory: the library allocates no device memory, frees none and
+ *    keeps no pointer past a call (BMINF page, 實現代碼分析2: the caller
+ *    allocates every output, the kernels only fill it).  The one call that
+ *    uses scratch memory, bq_gemm_splitk, takes it from the caller.
+ *  - Grid limits: a launch counts work-items per grid dimension and the
+ *    count must stay below 2^32; a shape whose launch would exceed it returns
+ *    BQ_ERR_SHAPE with nothing enqueued (e.g. bq_quantize_rows with 2^24 or
+ *    more rows, whose kernel runs 256 work-items per row).
+ *  - Thread safety: calls are reentrant; the only shared state is a cached
+ *    per-device property record, written once.
  */
 #ifndef BQ_H
 #define BQ_H
@@ -78,17 +74,18 @@ enum bq_status {
  * limit leaves a factor of two of headroom. */
 #define BQ_MAX_K 65536
 
-/* Largest M and N accepted by the GEMMs, and the largest output M * N.  The
- * launchers size their grids in 32-bit arithmetic and a launch holds at most
- * 2^31 - 1 workgroups; these bounds keep both exact.  An output at the limit
- * holds 2^42 elements (8 TiB in fp16), more than one device's memory. */
+/* Largest M and N accepted by the GEMMs, and the largest output M * N: the
+ * kernels index rows and tiles in 32-bit integers, which these bounds keep
+ * exact.  An output at the limit holds 2^42 elements (8 TiB in fp16), more
+ * than one device's memory.  Within them, a shape whose grid would exceed
+ * the dispatch limit (see the conventions) is rejected with BQ_ERR_SHAPE. */
 #define BQ_MAX_DIM (1LL << 30)
 #define BQ_MAX_OUT (1LL << 42)
 
 /* GEMM path selection for bq_gemm (the named GEMM calls use BQ_PATH_AUTO). */
 enum bq_path {
     BQ_PATH_AUTO = 0,   /* choose by M (see bq_gemm_select_path)              */
-    BQ_PATH_STREAM = 1, /* streaming skinny-M matrix-core kernel, M <= 64 (auto: M <= 32) */
+    BQ_PATH_STREAM = 1, /* streaming matrix-core kernel, M <= 256 (auto: 3 <= M <= 128, int2 <= 256) */
     BQ_PATH_TILED = 2,  /* LDS-tiled matrix-core kernel, any M                */
     BQ_PATH_GEMV = 3    /* decode GEMV on dot-product ALUs, M <= 4 (auto: M <= 2) */
 };
@@ -215,11 +212,46 @@ int bq_gemm_w2a8_i32(const int8_t *A, const uint8_t *B, int32_t *C_i32,
  *   bits       8, 4 or 2 (layout of B as above); BQ_ERR_ARG otherwise
  *   scale_f16  [N] fp16, or NULL for the int32 output
  *   C          fp16 [M, N] when scale_f16 != NULL, else int32 [M, N]
- *   path       enum bq_path; BQ_PATH_STREAM requires M <= 64, BQ_PATH_GEMV
+ *   path       enum bq_path; BQ_PATH_STREAM requires M <= 256, BQ_PATH_GEMV
  *              requires M <= 4 (BQ_ERR_SHAPE otherwise)
  */
 int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16,
             void *C, int64_t M, int64_t N, int64_t K, int path, void *stream);
+
+/*
+ * bq_gemm_splitk_workspace_bytes - device workspace bq_gemm_splitk uses to
+ * split K for this shape: 0 when it would not split (the output has more
+ * than 128 tiles of 64 x 64, or K is shorter than 1024), else 4096 bytes of
+ * per-tile counters plus 16 KiB of partial sums for each of the (at most
+ * 256) workgroups, at most 4 MiB + 4 KiB in all.  Negative: -BQ_ERR_ARG or
+ * -BQ_ERR_SHAPE for
+ * arguments bq_gemm would reject.  Host-only; no device call.
+ */
+int64_t bq_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
+
+/*
+ * bq_gemm_splitk - bq_gemm on the tiled kernel (BQ_PATH_TILED) with K split
+ * over several workgroups per output tile when the output has few tiles
+ * (Pallas matmul page, blocked matmul: the K blocks of one output block are
+ * independent partial sums; here up to 8 workgroups each sum a share of K,
+ * and the last of a tile to finish adds the others' int32 sums, which are
+ * exact, and runs the epilogue).  For shapes with few output tiles and long
+ * K, where one workgroup per tile would leave most CUs idle.
+ *
+ *   workspace        caller-owned device memory of workspace_bytes bytes,
+ *                    16-byte aligned; its first 4096 bytes must be zero
+ *                    before the first call (e.g. hipMemsetAsync), and every
+ *                    call leaves them zero again.  NULL with 0 bytes: K is
+ *                    not split.  Fewer bytes than
+ *                    bq_gemm_splitk_workspace_bytes(M, N, K, bits): K is not
+ *                    split (same results).
+ * Calls that share a workspace must not run concurrently (calls on one
+ * stream are ordered).  Other arguments, layouts and errors as for bq_gemm;
+ * a negative workspace_bytes gives BQ_ERR_SHAPE, a NULL workspace with a
+ * positive size BQ_ERR_NULL.
+ */
+int bq_gemm_splitk(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C, int64_t M,
+                   int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * bq_gemm_dual_scale - the GEMM of a linear layer whose activations were
@@ -319,8 +351,7 @@ int bq_gemm_act(const int8_t *A, const void *B, int bits, const void *w_scale_f1
  * K % 64 == 0 (BQ_ERR_SHAPE); pointers
  * 16-byte aligned (BQ_ERR_ALIGN); NULL where required (BQ_ERR_NULL).  M <= 4
  * runs a decode GEMV (dot products on the vector ALUs, a stream over B);
- * larger M the tiled matrix-core kernel (with the K split of the
- * conventions above when the output has few 64 x 64 tiles).
+ * larger M the tiled matrix-core kernel.
  */
 int bq_gemm_nf4_a16(const void *A_f16, const uint8_t *B, const void *scale_f16, const void *zero_f16,
                     void *C_f16, int64_t M, int64_t N, int64_t K, void *stream);

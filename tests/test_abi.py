@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -49,9 +49,12 @@ def test_select_path(bq):
     assert bq.select_path(1, 4096, 4096, 4) == "gemv"
     assert bq.select_path(2, 4096, 4096, 2) == "gemv"
     assert bq.select_path(3, 4096, 4096, 4) == "stream"
-    assert bq.select_path(32, 4096, 4096, 4) == "stream"
-    assert bq.select_path(33, 4096, 4096, 4) == "tiled"
-    assert bq.select_path(64, 12288, 4096, 8) == "tiled"
+    assert bq.select_path(64, 4096, 4096, 4) == "stream"
+    assert bq.select_path(64, 12288, 4096, 8) == "stream"
+    assert bq.select_path(128, 4096, 4096, 2) == "stream"
+    assert bq.select_path(129, 4096, 4096, 4) == "tiled"
+    assert bq.select_path(256, 4096, 4096, 2) == "stream"
+    assert bq.select_path(257, 4096, 4096, 2) == "tiled"
     assert bq.select_path(4096, 4096, 4096, 2) == "tiled"
 
 
@@ -79,8 +82,8 @@ def test_gemm_validation(bq):
     # the dimension and output limits are inclusive: the next check (NULL) decides
     assert L.bq_gemm(NULL, P16b, 8, P16c, P16d, 2**30, 4, 64, 0, S) == bq.BQ_ERR_NULL
     assert L.bq_gemm(NULL, P16b, 8, P16c, P16d, 2**21, 2**21, 64, 0, S) == bq.BQ_ERR_NULL
-    # the streaming kernel only takes M <= 64
-    assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 65, 4, 64, 1, S) == bq.BQ_ERR_SHAPE
+    # the streaming kernel only takes M <= 256
+    assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 257, 4, 64, 1, S) == bq.BQ_ERR_SHAPE
     # the GEMV path only takes M <= 4
     assert L.bq_gemm(P16, P16b, 8, P16c, P16d, 5, 4, 64, 3, S) == bq.BQ_ERR_SHAPE
     # nulls
@@ -97,6 +100,43 @@ def test_gemm_validation(bq):
     assert L.bq_gemm(NULL, NULL, 8, NULL, NULL, 0, 4, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm(NULL, NULL, 4, NULL, NULL, 4, 0, 64, 0, S) == bq.BQ_OK
     assert L.bq_gemm_w2a8_i32(NULL, NULL, NULL, 0, 0, 0, S) == bq.BQ_OK
+
+
+def test_splitk_workspace_bytes(bq):
+    """The workspace size follows the header's contract: 0 where K is not
+    split (more than 128 output tiles of 64 x 64, or K below 1024), else
+    4096 counter bytes plus 16 KiB per workgroup, at most 256 workgroups."""
+    f = bq.gemm_splitk_workspace_bytes
+    assert f(4096, 4096, 4096, 4) == 0          # 4096 tiles
+    assert f(64, 64 * 129, 4096, 8) == 0        # 129 tiles
+    assert f(64, 4096, 512, 4) == 0             # K too short to split
+    cap = 4096 + 256 * 16384
+    for bits in (8, 4, 2):
+        for M, N, K in [(64, 4096, 4096), (3, 40, 8192), (128, 512, 4160), (200, 300, 8192)]:
+            n = f(M, N, K, bits)
+            tiles = -(-M // 64) * -(-N // 64)
+            assert n > 4096 and (n - 4096) % 16384 == 0, (M, N, K, n)
+            wgs = (n - 4096) // 16384
+            assert wgs % tiles == 0 and 2 <= wgs // tiles <= 8 and wgs <= 256, (M, N, K, wgs)
+            assert n <= cap
+    assert f(0, 4096, 4096, 4) == 0
+    with pytest.raises(bq.BQError):
+        f(64, 64, 96, 4)
+    with pytest.raises(bq.BQError):
+        f(64, 64, 4096, 3)
+
+
+def test_splitk_validation(bq):
+    L = bq.lib()
+    S = NULL
+    f = L.bq_gemm_splitk
+    assert f(P16, P16b, 4, P16c, P16d, 64, 64, 4096, P16, -1, S) == bq.BQ_ERR_SHAPE
+    assert f(P16, P16b, 4, P16c, P16d, 64, 64, 4096, NULL, 4096, S) == bq.BQ_ERR_NULL
+    assert f(P16, P16b, 4, P16c, P16d, 64, 64, 4096, PODD, 4096, S) == bq.BQ_ERR_ALIGN
+    # the shared checks of bq_gemm apply
+    assert f(P16, P16b, 3, P16c, P16d, 64, 64, 4096, P16, 4096, S) == bq.BQ_ERR_ARG
+    assert f(P16, P16b, 4, P16c, P16d, 64, 64, 96, P16, 4096, S) == bq.BQ_ERR_SHAPE
+    assert f(NULL, NULL, 4, NULL, NULL, 0, 64, 4096, NULL, 0, S) == bq.BQ_OK
 
 
 def test_quantize_bits_validation(bq):

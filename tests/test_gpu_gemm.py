@@ -65,7 +65,9 @@ def _check(acc, C, A, Bv, s, rows=None, cols=None, what=""):
 
 SMALL = [(1, 16, 64), (1, 33, 128), (3, 100, 192), (16, 256, 256), (17, 48, 320),
          (33, 100, 320), (64, 520, 1024), (5, 4099, 128)]
-TILED_ONLY = [(65, 300, 384), (130, 257, 256), (257, 513, 640), (300, 130, 64)]
+# M up to 256 on the streaming and tiled paths; above 256 tiled only
+MID = [(65, 300, 384), (130, 257, 256), (256, 513, 640), (200, 130, 64)]
+TILED_ONLY = [(257, 513, 640), (300, 130, 64)]
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
@@ -75,6 +77,17 @@ def test_small_shapes_all_paths(dev, bits, path, shape):
     M, N, K = shape
     if path == "gemv" and M > 4:
         pytest.skip("the GEMV path takes M <= 4")
+    banner(f"gemm bits={bits} path={path} M={M} N={N} K={K}")
+    A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
+    acc, C = _run(dev, bits, A, Bp, s, path)
+    _check(acc, C, A, Bv, s, what=f"w{bits} {path} {shape}")
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("path", ["stream", "tiled", "auto"])
+@pytest.mark.parametrize("shape", MID)
+def test_mid_shapes(dev, bits, path, shape):
+    M, N, K = shape
     banner(f"gemm bits={bits} path={path} M={M} N={N} K={K}")
     A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
     acc, C = _run(dev, bits, A, Bp, s, path)
@@ -94,14 +107,15 @@ def test_small_shapes_tiled(dev, bits, shape):
 # Shapes that select each tile configuration of the tiled path, with ragged
 # M, N and K tails: 256x256 tiles (4100x4100), 128x128 (1030x4100), 64x64
 # with a 4-stage ring (1000x2100, K tail of 64) and 64x64 with an 8-stage ring
-# (the rest; 100x200x1088 has a K tail, 3x40x8192 a long K).
+# (the rest; 100x200x1088 has a K tail, 3x40x8192 a long K; none splits K:
+# bq_gemm passes no workspace).
 CFG_SHAPES = [(4100, 4100, 64), (1030, 4100, 128), (1000, 2100, 192), (200, 300, 1024),
               (100, 200, 1088), (3, 40, 8192), (130, 257, 256)]
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
 @pytest.mark.parametrize("shape", CFG_SHAPES)
-def test_tile_configs_and_split_k(dev, bits, shape):
+def test_tile_configs(dev, bits, shape):
     M, N, K = shape
     banner(f"gemm bits={bits} path=tiled M={M} N={N} K={K}")
     A, Bv, Bp, s = _make(bits, M, N, K, seed=M + N + K + bits)
@@ -128,36 +142,32 @@ def test_decode_gemv_w4a8_full(dev, N):
 
 @pytest.mark.parametrize("M", [1, 128])
 def test_ternary_w2a8_workload(dev, M):
+    """The ternary W2A8 workload at M = 1 and 128, N = K = 4096, every output
+    compared."""
     banner(f"gemm w2a8 ternary M={M} N=4096 K=4096")
     A, Bv, s = synth.w2a8_case(M, 4096, 4096, seed=0)
     acc, C = _run(dev, 2, A, oracle.pack_int2(Bv), s, "auto")
-    g = np.random.default_rng(1)
-    cols = np.sort(g.choice(4096, 512, replace=False))
-    _check(acc, C, A, Bv, s, cols=cols, what=f"w2a8 {M}x4096x4096")
+    _check(acc, C, A, Bv, s, what=f"w2a8 {M}x4096x4096")
 
 
 def test_bminf_quantize_then_w8a8(dev):
     """Quantized fused-QKV weight [12288, 4096] (codes and scales from the
-    oracle) times int8 activations, M=64."""
+    oracle) times int8 activations, M=64, every output compared."""
     banner("gemm w8a8 bminf M=64 N=12288 K=4096")
     W, A = synth.bminf_case()
     q, s = oracle.quantize_rows(W)
     acc, C = _run(dev, 8, A, q, s.view(np.float16), "auto")
-    g = np.random.default_rng(2)
-    cols = np.sort(np.concatenate([g.choice(12288, 1000, replace=False), [0, 12287]]))
-    _check(acc, C, A, q, s.view(np.float16), cols=np.unique(cols), what="w8a8 bminf")
+    _check(acc, C, A, q, s.view(np.float16), what="w8a8 bminf")
 
 
 @pytest.mark.parametrize("M", [1, 16, 64, 256, 1024, 4096])
 def test_w4a8_prefill_sweep(dev, M):
+    """The W4A8 sweep, N = K = 4096, every output compared (the M = 4096
+    oracle is one 4096^3 integer GEMM on the host cores, about 2 s)."""
     banner(f"gemm w4a8 sweep M={M} N=4096 K=4096")
     A, Bv, s = synth.w4a8_case(M, 4096, 4096, seed=0)
     acc, C = _run(dev, 4, A, oracle.pack_int4(Bv), s, "auto")
-    g = np.random.default_rng(M)
-    rows = np.arange(M) if M <= 64 else np.unique(np.concatenate(
-        [g.choice(M, 48, replace=False), [0, M - 1]]))
-    cols = np.unique(np.concatenate([g.choice(4096, 1024, replace=False), [0, 4095]]))
-    _check(acc, C, A, Bv, s, rows=rows, cols=cols, what=f"w4a8 sweep M={M}")
+    _check(acc, C, A, Bv, s, what=f"w4a8 sweep M={M}")
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
@@ -252,7 +262,7 @@ def test_error_paths(dev):
         bq.gemm(Au, torch.zeros((4, 64), dtype=torch.int8, device=dev), 8)
     assert e.value.status == bq.BQ_ERR_ALIGN
     with pytest.raises(bq.BQError) as e:
-        bq.gemm(torch.zeros((65, 64), dtype=torch.int8, device=dev),
+        bq.gemm(torch.zeros((257, 64), dtype=torch.int8, device=dev),
                 torch.zeros((4, 64), dtype=torch.int8, device=dev), 8, path="stream")
     assert e.value.status == bq.BQ_ERR_SHAPE
     with pytest.raises(bq.BQError) as e:
@@ -264,8 +274,9 @@ def test_error_paths(dev):
 @pytest.mark.parametrize("bits", [8, 4, 2])
 @pytest.mark.parametrize("N", [6143, 6144, 6145, 6200])
 def test_decode_gemv_rows_rule_boundary(dev, bits, N):
-    """M = 1 around the switch between one and two B rows per wavefront
-    (6144 rows per launch), K = 1024, compared in full."""
+    """M = 1 around the switch between one and several B rows per wavefront
+    (6144 rows per launch; ragged last wavefront above it), K = 1024,
+    compared in full."""
     banner(f"gemm decode rows-rule boundary bits={bits} N={N}")
     A, Bv, Bp, s = _make(bits, 1, N, 1024, seed=N + bits)
     acc, C = _run(dev, bits, A, Bp, s, "gemv")

@@ -3,9 +3,10 @@ the warm-up) and replayed: quantize -> pack -> GEMMs on every kernel path,
 with eager work and synchronizations between replays.  Every replay must give
 the eager results bit for bit (the kernels are deterministic), which also
 shows that no call of the path allocates, synchronizes or memsets inside the
-capture.  The tiled GEMM here splits K over workgroups (16 tiles, K = 1024),
-so the graph replays the split kernel with the stream's workspace, whose
-per-tile counters must reset themselves on every replay."""
+capture.  One call splits K over workgroups (bq_gemm_splitk, 16 tiles,
+K = 1024) with a workspace allocated and zeroed before the capture; the
+graph replays the split kernel on it, and its per-tile counters must reset
+themselves on every replay."""
 import numpy as np
 import pytest
 
@@ -35,6 +36,7 @@ def test_graph_replays_match_eager(dev):
         bq.pack_int4(q4, o["p4"])
         qx, sx = bq.quantize_rows(X, o["qx"], o["sx"])
         bq.gemm(qx, o["p4"], 4, s4, out=o["c_tiled"], path="tiled")
+        bq.gemm_splitk(qx, o["p4"], 4, s4, o["ws"], out=o["c_split"])
         bq.gemm_dual_scale(qx[:20], o["p4"], 4, s4, sx[:20], out=o["c_stream"], path="stream")
         bq.gemm(A1, o["p4"], 4, s4, out=o["c_gemv"], path="gemv")
         bq.gemm_act(qx, o["p4"], 4, s4, sx, act="gelu", out=o["c_act"])
@@ -47,6 +49,8 @@ def test_graph_replays_match_eager(dev):
             "qx": torch.empty((96, 1024), dtype=torch.int8, device=dev),
             "sx": torch.empty((96,), dtype=torch.float16, device=dev),
             "c_tiled": torch.empty((96, 512), dtype=torch.float16, device=dev),
+            "c_split": torch.empty((96, 512), dtype=torch.float16, device=dev),
+            "ws": torch.zeros(bq.gemm_splitk_workspace_bytes(96, 512, 1024, 4), dtype=torch.uint8, device=dev),
             "c_stream": torch.empty((20, 512), dtype=torch.float16, device=dev),
             "c_gemv": torch.empty((1, 512), dtype=torch.float16, device=dev),
             "c_act": torch.empty((96, 512), dtype=torch.float16, device=dev),
@@ -67,12 +71,17 @@ def test_graph_replays_match_eager(dev):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
         path(gbuf)
+    assert bq.gemm_splitk_workspace_bytes(96, 512, 1024, 4) > 0  # the call does split
     for rep in range(4):
-        for v in gbuf.values():  # poison the outputs between replays
-            v.zero_()
+        for k, v in gbuf.items():  # poison the outputs between replays
+            if k != "ws":
+                v.zero_()
         _ = (W.float() * 2).sum()  # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         for k, v in gbuf.items():
-            assert torch.equal(v.cpu(), ref[k]), f"replay {rep}: {k} differs from eager"
+            if k != "ws":
+                assert torch.equal(v.cpu(), ref[k]), f"replay {rep}: {k} differs from eager"
+        assert int(gbuf["ws"][:4096].count_nonzero()) == 0, "split-K counters not reset"
+    assert torch.equal(gbuf["c_split"], gbuf["c_tiled"])
