@@ -46,6 +46,7 @@ SIGNATURES = {
     "bq_gemm_nf4_a16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P],
     "bq_gemm_splitk_workspace_bytes": [_I64, _I64, _I64, _I],
     "bq_gemm_splitk": [_P, _P, _I, _P, _P, _I64, _I64, _I64, _P, _I64, _P],
+    "bq_gemm_splitk_static": [_P, _P, _I, _P, _P, _I64, _I64, _I64, _P],
 }
 _RESTYPES = {"bq_status_string": ctypes.c_char_p, "bq_gemm_splitk_workspace_bytes": ctypes.c_int64}
 
@@ -269,6 +270,16 @@ def gemm_splitk(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[tor
         nbytes = workspace.numel()
     _call("bq_gemm_splitk", dev, _ptr(A), _ptr(B), bits, _ptr(scale), _ptr(out), M, N, K, _ptr(workspace),
           nbytes)
+    return out
+
+
+def gemm_splitk_static(A: torch.Tensor, B: torch.Tensor, bits: int, scale: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm_splitk with the library's own static scratch (no device memory
+    is allocated by the call; pass `out` as well to allocate nothing here).
+    Calls that may overlap on one GPU race: order them on one stream."""
+    M, N, K, dev, out = _gemm_args(A, B, bits, scale, out)
+    _call("bq_gemm_splitk_static", dev, _ptr(A), _ptr(B), bits, _ptr(scale), _ptr(out), M, N, K)
     return out
 
 

@@ -10,6 +10,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/bq.h"
 #include "bq_internal.h"
@@ -255,6 +256,92 @@ int bq_gemm_splitk(const int8_t *A, const void *B, int bits, const void *scale_f
         return BQ_ERR_ALIGN;
     return gemm_common(A, B, bits, scale_f16, nullptr, 0, C, M, N, K, BQ_PATH_TILED, stream, 1, {},
                        workspace_bytes > 0 ? workspace : nullptr, workspace_bytes);
+}
+
+// ---- allocation-free split-K (bq_gemm_splitk_static) ----
+
+// Bytes of the library's own split-K scratch: the largest workspace any
+// shape asks for (4 KiB of per-tile counters, 16 KiB of partial sums for
+// each of at most 256 workgroups).
+constexpr int64_t kScratchBytes = 4096 + 256 * 16384;
+
+}  // extern "C"
+
+// The scratch memory of bq_gemm_splitk_static: one copy on every GPU the
+// library runs on, zero when the code object is loaded, held until the
+// process ends.  In host code `scratch` is not a device address; the kernels
+// receive the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return BQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return BQ_ERR_DEVICE;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return BQ_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BQ_OK;
+}
+
+// Zero n 32-bit words (a kernel, not a memset, so that a captured graph
+// replays it as a kernel node).
+__global__ void zero_words_kernel(int *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bq_gemm_splitk_static(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C, int64_t M,
+                          int64_t N, int64_t K, void *stream)
+{
+    int st = validate_gemm(A, B, bits, scale_f16, C, M, N, K, BQ_PATH_TILED);
+    if (st != BQ_OK || M == 0 || N == 0)
+        return st;
+    const int64_t need = bq::gemm_splitk_workspace_bytes((int)M, (int)N, (int)K, bits);
+    if (need > kScratchBytes)
+        return BQ_ERR_SHAPE;
+    st = check_device();
+    if (st != BQ_OK)
+        return st;
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_address(&ws);
+        if (st != BQ_OK)
+            return st;
+        // the per-tile counters start at zero whatever an earlier call left
+        constexpr int kCtrWords = 4096 / 4;
+        zero_words_kernel<<<kCtrWords / 256, 256, 0, (hipStream_t)stream>>>((int *)ws, kCtrWords);
+        st = launch_status(hipGetLastError());
+        if (st != BQ_OK)
+            return st;
+    }
+    return gemm_common(A, B, bits, scale_f16, nullptr, 0, C, M, N, K, BQ_PATH_TILED, stream, 1, {}, ws,
+                       ws ? kScratchBytes : 0);
 }
 
 // Largest batch of bq_gemm_batched (the grid's y dimension).

@@ -254,6 +254,25 @@ int bq_gemm_splitk(const int8_t *A, const void *B, int bits, const void *scale_f
                    int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * bq_gemm_splitk_static - bq_gemm_splitk with the library's own scratch
+ * instead of a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It allocates nothing: the scratch is a static device
+ * array of BQ_SPLITK_STATIC_BYTES (4 MiB + 4 KiB) that every GPU the library
+ * runs on holds until the process ends; its per-tile counters are cleared
+ * by a small kernel on `stream` before the GEMM.  A shape whose split would
+ * need more scratch than that returns BQ_ERR_SHAPE (no shape accepted by
+ * bq_gemm_splitk_workspace_bytes needs more).  Every call on one GPU shares
+ * that GPU's scratch: calls that may overlap (on different streams, or from
+ * different threads) race and give wrong results; order them on one stream.
+ * Results equal those of bq_gemm_splitk.  Other arguments, layouts and
+ * errors as for bq_gemm.
+ */
+#define BQ_SPLITK_STATIC_BYTES (4096LL + 256LL * 16384LL)
+int bq_gemm_splitk_static(const int8_t *A, const void *B, int bits, const void *scale_f16, void *C, int64_t M,
+                          int64_t N, int64_t K, void *stream);
+
+/*
  * bq_gemm_dual_scale - the GEMM of a linear layer whose activations were
  * quantized per token: A [M, K] holds the int8 codes of the M token rows
  * (bq_quantize_rows over the rows of the fp16 activations) and x_scale_f16

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(bq):
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     lib = ctypes.CDLL(bq.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -137,6 +137,24 @@ def test_splitk_validation(bq):
     assert f(P16, P16b, 3, P16c, P16d, 64, 64, 4096, P16, 4096, S) == bq.BQ_ERR_ARG
     assert f(P16, P16b, 4, P16c, P16d, 64, 64, 96, P16, 4096, S) == bq.BQ_ERR_SHAPE
     assert f(NULL, NULL, 4, NULL, NULL, 0, 64, 4096, NULL, 0, S) == bq.BQ_OK
+
+
+def test_splitk_static_validation(bq):
+    """The allocation-free entry point validates like bq_gemm before any
+    device call."""
+    L = bq.lib()
+    S = NULL
+    f = L.bq_gemm_splitk_static
+    assert f(P16, P16b, 3, P16c, P16d, 64, 64, 4096, S) == bq.BQ_ERR_ARG
+    assert f(P16, P16b, 4, P16c, P16d, 64, 64, 96, S) == bq.BQ_ERR_SHAPE
+    assert f(P16, P16b, 4, P16c, P16d, 64, 64, 65536 + 64, S) == bq.BQ_ERR_SHAPE
+    assert f(NULL, P16b, 4, P16c, P16d, 64, 64, 4096, S) == bq.BQ_ERR_NULL
+    assert f(PODD, P16b, 4, P16c, P16d, 64, 64, 4096, S) == bq.BQ_ERR_ALIGN
+    assert f(NULL, NULL, 4, NULL, NULL, 0, 64, 4096, S) == bq.BQ_OK
+    # every shape's split fits the static scratch (4 MiB + 4 KiB)
+    cap = 4096 + 256 * 16384
+    for M, N, K in [(64, 4096, 4096), (3, 40, 65536), (128, 8192, 65536), (1, 64 * 128, 65536)]:
+        assert bq.gemm_splitk_workspace_bytes(M, N, K, 8) <= cap
 
 
 def test_quantize_bits_validation(bq):
