@@ -18,29 +18,25 @@ FP16_MFMA_PEAK_FLOPS = 2.5e15
 FP32_VECTOR_PEAK_FLOPS = 157.3e12
 
 
-def matmul_flops(m: int, k: int, n: int) -> int:
-    """2*m*k*n, as on the Pallas page."""
-    return 2 * m * k * n
-
-
-def matmul_membw(m: int, k: int, n: int, itemsize: int) -> int:
-    """(m*k + k*n + m*n) * itemsize bytes, as on the Pallas page."""
-    return (m * k + k * n + m * n) * itemsize
-
-
 def gemm_ops(M: int, N: int, K: int) -> int:
-    return matmul_flops(M, K, N)
+    """Multiply-adds counted twice: 2 M N K."""
+    return 2 * M * N * K
+
+
+def operand_bytes(M: int, N: int, K: int, a_bytes: float, b_bits: int, out_bytes: int,
+                  scale_bytes: int = 0) -> int:
+    """Every operand moved once at its own width: A [M, K] at a_bytes per
+    element, B [N, K] at b_bits, a per-column scale [N] at scale_bytes, the
+    output [M, N] at out_bytes."""
+    return int(M * K * a_bytes) + (N * K * b_bits) // 8 + N * scale_bytes + M * N * out_bytes
 
 
 def gemm_bytes(M: int, N: int, K: int, bits: int, out: str = "f16") -> int:
     """A int8 [M,K] + B at `bits` [N,K] + fp16 scale [N] (f16 output only)
     + output [M,N] (fp16 or int32)."""
-    b = M * K + (N * K * bits) // 8
     if out == "f16":
-        b += 2 * N + 2 * M * N
-    else:
-        b += 4 * M * N
-    return b
+        return operand_bytes(M, N, K, 1, bits, 2, scale_bytes=2)
+    return operand_bytes(M, N, K, 1, bits, 4)
 
 
 def nf4_gemm_bytes(M: int, N: int, K: int, zero: bool = True) -> int:

@@ -3,11 +3,11 @@ fused-activation section: the activation applied once to the wide result of
 the last K step, then one downcast; BladeDISC page: GEMM + GELU fusion).
 
 GELU is v * Phi(v) with Phi the standard normal CDF, evaluated as
-erfc(-v / sqrt(2)) / 2.  Independent checks: CPython's own math.erfc (not the
-C library's) and scipy's erfc, printed values of Phi, the identity
-GELU(-v) = GELU(v) - v, and for ReLU the exact clamp of numpy's product."""
-import math
-
+erfc(-v / sqrt(2)) / 2.  Independent checks: mpmath's erfc at 50 significant
+digits (arbitrary precision, no C library involved), scipy's erfc, printed
+values of Phi, the identity GELU(-v) = GELU(v) - v, and for ReLU the exact
+clamp of numpy's product."""
+import mpmath
 import numpy as np
 import pytest
 from scipy import special
@@ -15,11 +15,28 @@ from scipy import special
 from bit_mixed_precision_amd import synth
 
 
-def test_gelu_matches_python_erfc(oracle):
-    for v in [-40.0, -12.5, -5.0, -1.7, -1e-3, -1e-30, 0.0, 1e-30, 2e-3, 0.5, 3.25, 9.0, 40.0]:
-        ref = 0.5 * v * math.erfc(-v / math.sqrt(2.0))
+def _gelu_mp(v: float) -> float:
+    """GELU at 50 significant digits, rounded once to double."""
+    with mpmath.workdps(50):
+        x = mpmath.mpf(v)
+        return float(x * mpmath.erfc(-x / mpmath.sqrt(2)) / 2)
+
+
+def test_gelu_matches_arbitrary_precision_erfc(oracle):
+    """Close to the 50-digit value, also far into the negative tail where
+    erfc is tiny (there 1 - erf would lose every digit).  Tolerance: the
+    double argument -v/sqrt(2) carries a relative rounding error of about
+    1e-16, which erfc's slope (-2x erfc(x) per unit of x) turns into a
+    relative error of about 2x^2 1e-16 of the result, 1e-13 at v = -37; the
+    result is then rounded to fp16 (relative 5e-4)."""
+    for v in [-37.0, -25.0, -12.5, -8.0, -5.0, -1.7, -1e-3, -1e-30, 0.0, 1e-30, 2e-3, 0.5, 3.25, 9.0, 40.0]:
+        ref = _gelu_mp(v)
         got = oracle.act(v, "gelu")
-        assert got == pytest.approx(ref, rel=1e-14, abs=1e-300), v
+        assert got == pytest.approx(ref, rel=1e-12, abs=1e-320), v
+        if abs(v) < 3:
+            assert got == pytest.approx(ref, rel=2e-15, abs=1e-320), v
+    # in the tail the value is nonzero and tiny: GELU(-12.5) ~ -1e-35
+    assert -1e-34 < oracle.act(-12.5, "gelu") < -1e-36
 
 
 def test_gelu_printed_cdf_values_and_symmetry(oracle):

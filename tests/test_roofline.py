@@ -20,13 +20,16 @@ def _golden():
 
 
 def test_pallas_worked_values():
+    """With every operand at one width the model is the page's: 2 m k n
+    operations and (m k + k n + m n) * itemsize bytes at 1024^3 in f32."""
     g = _golden()
-    assert roofline.matmul_flops(1024, 1024, 1024) == g["matmul_flops_1024_1024_1024"]
-    assert roofline.matmul_membw(1024, 1024, 1024, 4) == g["matmul_membw_1024_1024_1024_f32"]
-    i32 = roofline.matmul_flops(1024, 1024, 1024) / roofline.matmul_membw(1024, 1024, 1024, 4)
-    i16 = roofline.matmul_flops(1024, 1024, 1024) / roofline.matmul_membw(1024, 1024, 1024, 2)
-    assert i32 == pytest.approx(g["intensity_1024_f32_approx"], abs=0.05)
-    assert i16 == pytest.approx(g["intensity_1024_bf16_approx"], abs=0.5)
+    ops = roofline.gemm_ops(1024, 1024, 1024)
+    b32 = roofline.operand_bytes(1024, 1024, 1024, 4, 32, 4)
+    b16 = roofline.operand_bytes(1024, 1024, 1024, 2, 16, 2)
+    assert ops == g["matmul_flops_1024_1024_1024"]
+    assert b32 == g["matmul_membw_1024_1024_1024_f32"]
+    assert ops / b32 == pytest.approx(g["intensity_1024_f32_approx"], abs=0.05)
+    assert ops / b16 == pytest.approx(g["intensity_1024_bf16_approx"], abs=0.5)
     assert g["v5e_flops"] / g["v5e_membw"] == pytest.approx(g["v5e_ridge_approx"], abs=0.05)
     # square f32 matmul crosses the v5e ridge at m = k = n ~ 1440: 2m^3 / 12m^2 = 240
     m = g["square_crossover_f32"]
