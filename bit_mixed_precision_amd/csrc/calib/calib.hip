@@ -6,7 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
+namespace bq {
+namespace calib {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const uint4 *__restric
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
 }
 
-}  // namespace
+}  // namespace calib
+}  // namespace bq
 
 extern "C" {
 
@@ -57,7 +59,7 @@ int bq_calib_mfma_loop(int blocks, int iters, int *out, void *stream)
 {
     if (blocks <= 0 || iters < 0 || !out)
         return (int)hipErrorInvalidValue;
-    mfma_loop_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(iters, out);
+    bq::calib::mfma_loop_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(iters, out);
     return (int)hipGetLastError();
 }
 
@@ -67,7 +69,7 @@ int bq_calib_read_stream(const void *buf, int64_t bytes, int blocks, uint32_t *o
 {
     if (blocks <= 0 || bytes < 0 || bytes % 16 != 0 || !buf || !out || ((uintptr_t)buf & 15) != 0)
         return (int)hipErrorInvalidValue;
-    read_stream_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(
+    bq::calib::read_stream_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(
         (const uint4 *)buf, bytes / 16, out);
     return (int)hipGetLastError();
 }

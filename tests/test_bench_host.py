@@ -57,3 +57,30 @@ def test_traffic_summary_follows_the_source_hash(monkeypatch):
     # a source change (a different hash) voids the summary
     monkeypatch.setattr(b, "tiled_source_hash", lambda: "0" * 16)
     assert b.measured_traffic() is None
+
+
+def test_trace_durations_pairs_labels_with_bench_dispatches(tmp_path):
+    """The kernel-trace parser keeps only the library's and calibration
+    kernels (namespace bq), in dispatch order, pairs them one to one with the
+    trace child's labels, and refuses a count mismatch."""
+    b = _bench()
+    rows = [  # (dispatch id, name, start ns, end ns), out of order on purpose
+        (3, "void bq::(anonymous namespace)::gemv_kernel<4, 1, 1, 4, 2, true>(...)", 5000, 9500),
+        (1, "void bq::(anonymous namespace)::quantize_rows_vec<2>(...)", 1000, 31000),
+        (2, "void at::native::vectorized_elementwise_kernel<...>", 31000, 31500),
+        (4, "void bq::calib::read_stream_kernel(uint4 const*, long, unsigned int*)", 10000, 14000),
+        (5, "void bq::(anonymous namespace)::gemv_kernel<4, 1, 1, 4, 2, true>(...)", 20000, 24500),
+    ]
+    p = tmp_path / "bench_kernel_trace.csv"
+    with open(p, "w") as fh:
+        fh.write('"Kind","Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for d, n, s, e in rows:
+            fh.write(f'"KERNEL_DISPATCH",{d},"{n}",{s},{e}\n')
+    got = b.trace_durations(str(p), ["quantize_rows", "gemm_w4a8_m1", "read", "gemm_w4a8_m1"])
+    assert got == {"quantize_rows": [30.0], "gemm_w4a8_m1": [4.5, 4.5], "read": [4.0]}
+    import pytest
+
+    with pytest.raises(ValueError):
+        b.trace_durations(str(p), ["quantize_rows", "gemm_w4a8_m1"])
+    st = b.stats([1.0, 2.0, 3.0, 4.0, 100.0])
+    assert st["us"] == 3.0 and st["n"] == 5 and st["us_min"] == 1.0
