@@ -10,12 +10,16 @@
 //  * one wavefront per R consecutive rows of B; its 64 lanes walk each packed
 //    row in 16-byte chunks (lane l takes chunks l, l + 64, ...), so one load
 //    instruction covers 1 KB of a row;
-//  * every load of a lane (its chunks of all R rows, and the bytes of A
-//    they multiply, which are the same for every row and are loaded once) is
-//    issued before any is used, and the weight scale of the output the lane
-//    writes just before them, so no memory latency follows the stream;
-//  * packed values are unpacked in registers to 16 v / 64 v bytes (unpack.h)
-//    and multiplied with v_dot4_i32_i8;
+//  * the bytes of A a pass multiplies are the same for every wavefront of
+//    the workgroup: wavefront 0 brings them into LDS with the LDS-DMA form
+//    of the 16-byte buffer load (1 KB of consecutive bytes per instruction),
+//    and after a barrier every lane reads its slice from there; every B load
+//    of a lane (its chunks of all R rows) is issued before any is used, and
+//    the weight scale of the output the lane writes just before them, so no
+//    memory latency follows the stream;
+//  * packed values are unpacked in registers to 16 v / 64 v bytes with
+//    shifts and masks only, the A bytes permuted to match once per chunk for
+//    all R rows, and multiplied with v_dot4_i32_i8;
 //  * the R x MR lane sums are reduced across the wavefront by a butterfly that
 //    halves the number of values at each of the first log2(R MR) steps (each
 //    lane keeps the half its partner does not, and adds the partner's copy of
@@ -26,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include "bq_internal.h"
+#include "lds_dma.h"
 #include "unpack.h"
 
 namespace bq {
@@ -41,6 +46,72 @@ __device__ __forceinline__ int row_sum16(int v)
     v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
     v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
     return v;
+}
+
+// Packed B bytes of one 16-byte chunk as dot-product operands, without the
+// byte permutes that would restore k order (the A bytes are permuted to
+// match instead, once per chunk for all the rows of a wavefront).  Values sit
+// in the high bits of their bytes (16 v for int4, 64 v for int2, as in
+// unpack.h), so each product is exact and the sums are 2^kShift times the
+// true ones:
+//  * int4, dword d of the chunk (k = 8d ... 8d + 7): o[2d] byte b holds
+//    k = 8d + 2b, o[2d + 1] byte b holds k = 8d + 2b + 1;
+//  * int2, dword d (k = 16d ... 16d + 15): o[4d + j] byte b holds
+//    k = 16d + 4b + j (code v + 2 turned into v by flipping its high bit);
+//  * int8: the bytes as they are.
+template <int BITS>
+__device__ __forceinline__ void unpack_b(const uint4 &p, uint32_t *o)
+{
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        if constexpr (BITS == 8) {
+            o[d] = w[d];
+        } else if constexpr (BITS == 4) {
+            o[2 * d] = (w[d] << 4) & 0xF0F0F0F0u;
+            o[2 * d + 1] = w[d] & 0xF0F0F0F0u;
+        } else {
+            const uint32_t x = w[d] ^ 0xAAAAAAAAu;
+            o[4 * d] = (x << 6) & 0xC0C0C0C0u;
+            o[4 * d + 1] = (x << 4) & 0xC0C0C0C0u;
+            o[4 * d + 2] = (x << 2) & 0xC0C0C0C0u;
+            o[4 * d + 3] = x & 0xC0C0C0C0u;
+        }
+    }
+}
+
+// The A bytes of a 16-byte packed B chunk (16 * 8 / BITS of them, in k
+// order) rearranged to pair with unpack_b's operands.
+template <int BITS>
+__device__ __forceinline__ void order_a(const uint4 *a, uint32_t *ap)
+{
+    constexpr int kD = 16 * 8 / BITS / 4;  // A dwords per chunk
+    uint32_t w[kD];
+#pragma unroll
+    for (int h = 0; h < kD / 4; ++h) {
+        w[4 * h] = a[h].x, w[4 * h + 1] = a[h].y, w[4 * h + 2] = a[h].z, w[4 * h + 3] = a[h].w;
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        if constexpr (BITS == 8) {
+            ap[d] = w[d];
+        } else if constexpr (BITS == 4) {
+            // even k (8d, 8d + 2, 8d + 4, 8d + 6) and odd k of A dwords 2d, 2d + 1
+            ap[2 * d] = __builtin_amdgcn_perm(w[2 * d + 1], w[2 * d], 0x06040200u);
+            ap[2 * d + 1] = __builtin_amdgcn_perm(w[2 * d + 1], w[2 * d], 0x07050301u);
+        } else {
+            // 4 x 4 byte transpose of A dwords 4d .. 4d + 3: ap[4d + j] byte b
+            // = A[16d + 4b + j]
+            const uint32_t t0 = __builtin_amdgcn_perm(w[4 * d + 1], w[4 * d], 0x05010400u);
+            const uint32_t t1 = __builtin_amdgcn_perm(w[4 * d + 1], w[4 * d], 0x07030602u);
+            const uint32_t t2 = __builtin_amdgcn_perm(w[4 * d + 3], w[4 * d + 2], 0x05010400u);
+            const uint32_t t3 = __builtin_amdgcn_perm(w[4 * d + 3], w[4 * d + 2], 0x07030602u);
+            ap[4 * d] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+            ap[4 * d + 1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+            ap[4 * d + 2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+            ap[4 * d + 3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+        }
+    }
 }
 
 // MR rows of A, R rows of B per wavefront, WAVES wavefronts per workgroup,
@@ -67,14 +138,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     }
     using Up = Unpack<BITS>;
     constexpr int kAPerChunk = 16 * 8 / BITS;  // bytes of A (= k values) per packed chunk
+    constexpr int kAPass = 64 * U * kAPerChunk;  // bytes of one A row per pass (4 KB)
+    static_assert(kAPass % 1024 == 0, "whole 1 KB DMA blocks");
+    // the A bytes of a pass, two passes deep: the same for every wavefront
+    __shared__ __attribute__((aligned(1024))) uint8_t As[2][MR][kAPass];
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = (blockIdx.x * WAVES + wave) * R;
-    if (n0 >= N)
-        return;
     const int64_t rowBytes = (int64_t)K * BITS / 8;
     const int chunks = (int)(rowBytes / 16);  // K % 64 == 0: whole chunks
-    const uint8_t *brow = B + (int64_t)n0 * rowBytes;
+    // a wavefront past N loads and stores nothing but takes part in every
+    // barrier (wavefront 0, which moves A, is never past N)
+    if (n0 >= N) {
+        for (int c0 = 0; c0 < chunks; c0 += 64 * U)
+            __syncthreads();
+        return;
+    }
+    // B rows past N are read from the last row (their sums are not stored)
+    const uint8_t *brow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        brow[r] = B + (int64_t)min(n0 + r, N - 1) * rowBytes;
 
     int acc[MR][R];
 #pragma unroll
@@ -87,53 +172,77 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     // loaded first: its latency overlaps the stream's
     const int myV = lane >> (6 - kLogV);  // sum index m * R + r held at the end
     const int myM = myV / R, myN = n0 + myV % R;
-    float sc = 1.0f;
-    if (F16OUT && myM < M && myN < N) {
-        sc = __half2float(__ushort_as_half(scale[myN]));
-        if (xscale)
-            sc *= __half2float(__ushort_as_half(xscale[myM]));  // exact in fp32
+    // (clamped indices, no branch: no wait until the value is used)
+    uint16_t scBits = 0, xsBits = 0;
+    if constexpr (F16OUT) {
+        scBits = scale[min(myN, N - 1)];
+        xsBits = (xscale ? xscale : scale)[xscale ? min(myM, M - 1) : 0];
     }
+    // per-lane DMA offsets within a pass (the pass's offset goes in the
+    // scalar operand)
+    uint32_t dmaOff[kAPass / 1024];
+#pragma unroll
+    for (int d = 0; d < kAPass / 1024; ++d)
+        dmaOff[d] = 1024u * d + 16u * lane;
 
-    for (int c0 = 0; c0 < chunks; c0 += 64 * U) {
-        uint4 b[R][U];
-        uint4 a[MR][U][kAPerChunk / 16];
+    for (int c0 = 0, pass = 0; c0 < chunks; c0 += 64 * U, ++pass) {
+        uint8_t(*as)[kAPass] = As[pass & 1];
+        // A of this pass into LDS: wavefront 0, coalesced 1 KB DMA blocks
+        // (k past K reads as zeros); issued before its B loads, so that its
+        // wait for the B loads' count leaves only them in flight
+        if (wave == 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + lane + 64 * u;
-            const bool ok = c < chunks;
+            for (int m = 0; m < MR; ++m) {
+                if (m < M) {
+                    const v4si ra = make_rsrc(A + (int64_t)m * K, (uint32_t)K);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const bool rok = ok && (n0 + r) < N;
-                b[r][u] = rok ? load_nt16(brow + (int64_t)r * rowBytes + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
+                    for (int d = 0; d < kAPass / 1024; ++d)
+                        dma16(ra, lds_addr(&as[m][1024 * d]), dmaOff[d], (uint32_t)(c0 * kAPerChunk));
+                }
             }
         }
+        // B: every lane issues all its loads (clamped addresses, so the
+        // count is fixed)
+        uint4 b[R][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + lane + 64 * u;
-            const bool ok = c < chunks;
+            const int c = min(c0 + lane + 64 * u, chunks - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                b[r][u] = *(const uint4 *)(brow[r] + (int64_t)c * 16);
+        }
+        if (wave == 0)
+            wait_vmcnt<R * U>();  // the A DMA has landed
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // chunks past the row: A reads as zero there (the DMA's range), so
+            // the clamped B chunk adds nothing
+            uint4 a[MR][kAPerChunk / 16];
 #pragma unroll
             for (int m = 0; m < MR; ++m)
 #pragma unroll
                 for (int h = 0; h < kAPerChunk / 16; ++h)
-                    a[m][u][h] = (ok && m < M) ? *(const uint4 *)(A + (int64_t)m * K + (int64_t)c * kAPerChunk + 16 * h)
-                                               : make_uint4(0, 0, 0, 0);
-        }
+                    a[m][h] = m < M ? *(const uint4 *)&as[m][(lane + 64 * u) * kAPerChunk + 16 * h]
+                                    : make_uint4(0, 0, 0, 0);
+            // the A bytes of the chunk in the order the packed B bytes unpack
+            // in (once per chunk, shared by the wavefront's R rows)
+            uint32_t ap[MR][kAPerChunk / 4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+            for (int m = 0; m < MR; ++m)
+                order_a<BITS>(a[m], ap[m]);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                uint32_t o[Up::kOutDwords];
-                Up::run(b[r][u], o);
+                uint32_t o[kAPerChunk / 4];
+                unpack_b<BITS>(b[r][u], o);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     // two independent chains of dot products
                     int s0 = acc[m][r], s1 = 0;
 #pragma unroll
-                    for (int h = 0; h < kAPerChunk / 16; ++h) {
-                        s0 = __builtin_amdgcn_sdot4((int)a[m][u][h].x, (int)o[4 * h + 0], s0, false);
-                        s1 = __builtin_amdgcn_sdot4((int)a[m][u][h].y, (int)o[4 * h + 1], s1, false);
-                        s0 = __builtin_amdgcn_sdot4((int)a[m][u][h].z, (int)o[4 * h + 2], s0, false);
-                        s1 = __builtin_amdgcn_sdot4((int)a[m][u][h].w, (int)o[4 * h + 3], s1, false);
+                    for (int i = 0; i < kAPerChunk / 4; i += 2) {
+                        s0 = __builtin_amdgcn_sdot4((int)ap[m][i], (int)o[i], s0, false);
+                        s1 = __builtin_amdgcn_sdot4((int)ap[m][i + 1], (int)o[i + 1], s1, false);
                     }
                     acc[m][r] = s0 + s1;
                 }
@@ -182,8 +291,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     // the first lane holding each sum writes it
     if ((lane & ((64 >> kLogV) - 1)) == 0 && myM < M && myN < N) {
         const int x = sum >> Up::kShift;  // exact: a multiple of 2^kShift
-        if (F16OUT)
+        if (F16OUT) {
+            float sc = __half2float(__ushort_as_half(scBits));
+            if (xscale)
+                sc *= __half2float(__ushort_as_half(xsBits));  // exact in fp32
             ((__half *)C)[(int64_t)myM * N + myN] = __float2half_rn(apply_act((float)x * sc, act));
+        }
         else
             ((int *)C)[(int64_t)myM * N + myN] = x;
     }
@@ -213,31 +326,35 @@ hipError_t launch_cfg(int idx, const int8_t *A, const uint8_t *B, const uint16_t
     // a lane's chunks per row per pass: 64 * U chunks cover K = 4096
     constexpr int U = BITS == 8 ? 4 : BITS == 4 ? 2 : 1;
     switch (idx) {
-    case 0: return launch_t<BITS, MR, 1, 4, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 1: return launch_t<BITS, MR, 2, 4, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 2: return launch_t<BITS, MR, 4, 4, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 3: return launch_t<BITS, MR, 8, 4, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 4: return launch_t<BITS, MR, 2, 8, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 5: return launch_t<BITS, MR, 4, 8, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    case 6: return launch_t<BITS, MR, 4, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
-    default: return launch_t<BITS, MR, 8, 2, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 0: return launch_t<BITS, MR, 1, 8, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 1: return launch_t<BITS, MR, 1, 16, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    case 2: return launch_t<BITS, MR, 2, 4, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
+    default: return launch_t<BITS, MR, 2, 8, U>(A, B, scale, xscale, act, C, M, N, K, batch, bs, s);
     }
 }
 
 // Measured on MI355X (kernel trace, K = 4096, each launch on a different B
-// past the caches): at M = 1 one row per wavefront up to 6144 rows per
-// launch (int4 N = 4096: 4.48 us against 4.54 / 4.56 for two / four rows),
-// four rows above that (int4 N = 11008: 6.84 against 7.60 with one; int8
-// two: 9.58 against 9.66); at M = 2 two rows (4.84 / 7.70 us for int4).
+// past the caches; shapes 1x8, 1x16, 2x4, 2x8, 4x2, 4x4, 4x8 and 8x4 tried):
+//   int2: two rows, eight wavefronts (M = 1: 3.48 us at N = 4096, 5.00 at
+//         11008; M = 4: 5.38 / 9.38);
+//   int4: up to 6144 rows one row, sixteen wavefronts (M = 1: 3.76 us at
+//         N = 4096, the time of a plain read of the same 8.4 MB); above
+//         that two rows, eight wavefronts (6.12 at N = 11008), four for
+//         M >= 3 (10.70 against 11.02);
+//   int8: one row; sixteen wavefronts up to 6144 rows for M <= 2 (4.68 us),
+//         else eight (8.98 at N = 11008); two rows, four wavefronts for
+//         M >= 3 above 6144 rows (11.90).
+// Four or eight rows per wavefront were slower at M > 1 in every case.
 int choose_cfg(int M, int N, int bits, int batch)
 {
-    const int64_t rows = (int64_t)N * batch;
-    if (M == 1) {
-        if (rows <= 6144)
-            return 0;
-        return bits == 8 ? 1 : 2;
-    }
-    return 1;
+    const bool small = (int64_t)N * batch <= 6144;
+    if (bits == 2)
+        return 3;
+    if (bits == 4)
+        return small ? 1 : M >= 3 ? 2 : 3;
+    if (small)
+        return M <= 2 ? 1 : 0;
+    return M <= 2 ? 0 : 2;
 }
 
 template <int BITS>

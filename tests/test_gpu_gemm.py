@@ -272,21 +272,23 @@ def test_error_paths(dev):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("M", [1, 2, 4])
 @pytest.mark.parametrize("N", [6143, 6144, 6145, 6200])
-def test_decode_gemv_rows_rule_boundary(dev, bits, N):
-    """M = 1 around the switch between one and several B rows per wavefront
-    (6144 rows per launch; ragged last wavefront above it), K = 1024,
+def test_decode_gemv_rows_rule_boundary(dev, bits, M, N):
+    """Around the 6144-rows-per-launch switch between wavefront shapes (one or
+    two B rows per wavefront, four to sixteen wavefronts per workgroup, by
+    bits and M; ragged last workgroup with idle wavefronts), K = 1024,
     compared in full."""
-    banner(f"gemm decode rows-rule boundary bits={bits} N={N}")
-    A, Bv, Bp, s = _make(bits, 1, N, 1024, seed=N + bits)
+    banner(f"gemm decode rows-rule boundary bits={bits} M={M} N={N}")
+    A, Bv, Bp, s = _make(bits, M, N, 1024, seed=N + bits + 7 * M)
     acc, C = _run(dev, bits, A, Bp, s, "gemv")
-    _check(acc, C, A, Bv, s, what=f"w{bits} gemv 1x{N}x1024")
+    _check(acc, C, A, Bv, s, what=f"w{bits} gemv {M}x{N}x1024")
 
 
 @pytest.mark.parametrize("bits", [4, 2])
 def test_decode_gemv_batched_rows_rule(dev, bits):
     """Batched M = 1 GEMV where N x batch crosses the 6144-row switch
-    (3 x 2112 = 6336 rows: two rows per wavefront; 2 x 2112: one; 2112 keeps
+    (3 x 2112 = 6336 rows and 2 x 2112 fall on either side of it; 2112 keeps
     every batch's scale and output 16-byte aligned)."""
     import torch
 
