@@ -55,6 +55,8 @@ STEP_NAMES = ["quantize_rows", "gemm_w8a8_m64", "pack_int4", "gemm_w4a8_m1",
               "gemm_w4a8_m4096", "pack_int2", "gemm_w2a8_m1", "gemm_w2a8_m128"]
 # same-size cold reads beside the decode GEMVs (algorithmic bytes of W2A8 and
 # W4A8 at M = 1, N = K = 4096, and W4A8 at N = 11008)
+# iterations of the W4A8-data matrix-core loop (32 instructions each)
+STREAM_ITERS = 500
 READ_SIZES = {"gemm_w2a8_m1": 4214784, "gemm_w4a8_m1": 8409088, "gemm_w4a8_m1_n11008": 22592512}
 
 
@@ -457,6 +459,11 @@ def child(args):
         if rc != 0:
             raise RuntimeError(f"bq_calib_mfma_loop: hip error {rc}")
 
+    def mfma_w4a8_stream(i):
+        rc = calib.bq_calib_mfma_w4a8_stream(loop_blocks, STREAM_ITERS, ctypes.c_void_p(cal_out.data_ptr()), cstream)
+        if rc != 0:
+            raise RuntimeError(f"bq_calib_mfma_w4a8_stream: hip error {rc}")
+
     rd_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
 
     def reader(nbytes, blocks):
@@ -472,6 +479,7 @@ def child(args):
         return fn
 
     timed("mfma_i8_loop", mfma_loop, reps=10, warm=2)
+    timed("mfma_i8_loop_w4a8_data", mfma_w4a8_stream, reps=10, warm=2)
     timed("read_stream_1GiB", reader(1 << 30, 2048), reps=10, warm=2)
     for key, nbytes in READ_SIZES.items():
         timed(f"read_{nbytes}", reader(nbytes, 2048))
@@ -832,6 +840,8 @@ def build_line(args, meas, trace, why):
 
     loop_us = primary("mfma_i8_loop", ev.get("mfma_i8_loop"))[0]
     loop_tops = 1024 * 4 * 4000 * 4 * 65536 / (loop_us * 1e-6) / 1e12
+    data_us = primary("mfma_i8_loop_w4a8_data", ev.get("mfma_i8_loop_w4a8_data"))[0]
+    data_tops = 1024 * 4 * STREAM_ITERS * 32 * 65536 / (data_us * 1e-6) / 1e12
     rd_us = primary("read_stream_1GiB", ev.get("read_stream_1GiB"))[0]
     rd_gbs = (1 << 30) / (rd_us * 1e-6) / 1e9
     ceilings = {
@@ -841,7 +851,14 @@ def build_line(args, meas, trace, why):
                              "frac_of_hbm_peak": round(rd_gbs * 1e9 / roofline.HBM_PEAK_BYTES_PER_S, 4)},
         "read_same_size": {str(nb): {"us": read_us(nb), "GB_per_s": round(nb / (read_us(nb) * 1e-6) / 1e9, 1)}
                            for nb in READ_SIZES.values()},
+        # the W4A8 GEMM's matrix-core instruction stream on operands drawn like
+        # the workload's: the clock the matrix cores hold depends on the bits
+        # they multiply, so this, not the constant-operand loop, is the
+        # matrix-core rate the GEMM can reach on this data
+        "mfma_i8_loop_w4a8_data": {"us": round(data_us, 2), "TOPS": round(data_tops, 2),
+                                   "frac_of_int8_peak": round(data_tops * 1e12 / roofline.INT8_MFMA_PEAK_OPS_PER_S, 4)},
         "value_frac_of_mfma_loop": round(head["TOPS"] / loop_tops, 4),
+        "value_frac_of_mfma_w4a8_data_loop": round(head["TOPS"] / data_tops, 4),
     }
     if "device_copy_512MiB" in ev:
         cp_us = ev["device_copy_512MiB"]

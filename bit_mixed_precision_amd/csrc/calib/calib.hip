@@ -33,6 +33,62 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, int *__restri
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The matrix-core instruction stream of the W4A8 GEMM's 128-k stage with no
+// memory traffic: four 32-k sub-steps, each 2 B operands x 4 A operands into
+// 8 accumulators, on operands drawn like the workload's (A bytes uniform in
+// [-127, 127], B bytes 16 v with v uniform in [-8, 7], as the kernels feed
+// unpacked int4).  The matrix cores' power, and with it the clock they hold,
+// depends on the operand bits; constant operands (mfma_loop_kernel) keep the
+// clock far higher than such data does.
+__global__ __launch_bounds__(256) void mfma_w4a8_stream_kernel(int iters, int *__restrict__ out)
+{
+    uint32_t h = (uint32_t)(blockIdx.x * blockDim.x + threadIdx.x) * 2654435761u + 0x9E3779B9u;
+    auto next = [&h]() {  // xorshift32
+        h ^= h << 13;
+        h ^= h >> 17;
+        h ^= h << 5;
+        return h;
+    };
+    v4i a[4][4], b[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    w |= (uint32_t)(uint8_t)(int8_t)((int)(next() % 255u) - 127) << (8 * q);
+                a[ks][i][e] = (int)w;
+            }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                b[ks][j][e] = (int)(next() & 0xF0F0F0F0u);
+    }
+    v16i c[4][2] = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[ks][j], a[ks][i], c[i][j], 0, 0, 0);
+    }
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                s ^= c[i][j][e];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // Grid-stride read of n16 16-byte words with nontemporal loads; each thread
 // stores the XOR of what it read.
 __global__ __launch_bounds__(256) void read_stream_kernel(const uint4 *__restrict__ p, int64_t n16,
@@ -60,6 +116,16 @@ int bq_calib_mfma_loop(int blocks, int iters, int *out, void *stream)
     if (blocks <= 0 || iters < 0 || !out)
         return (int)hipErrorInvalidValue;
     bq::calib::mfma_loop_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(iters, out);
+    return (int)hipGetLastError();
+}
+
+// blocks x 256 threads, 32 matrix instructions per iteration per wavefront;
+// `out` holds blocks * 256 ints.  Returns a hipError_t.
+int bq_calib_mfma_w4a8_stream(int blocks, int iters, int *out, void *stream)
+{
+    if (blocks <= 0 || iters < 0 || !out)
+        return (int)hipErrorInvalidValue;
+    bq::calib::mfma_w4a8_stream_kernel<<<dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream>>>(iters, out);
     return (int)hipGetLastError();
 }
 

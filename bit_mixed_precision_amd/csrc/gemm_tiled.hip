@@ -223,6 +223,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     }
     using U = Unpack<BITS>;
     using T = TiledCfg<BITS, BM, BN, STAGES, F16OUT, WAVES, NF4, WGM>;
+    // the ping-pong loop below: eight wavefronts (two per SIMD) in a 2 x 4
+    // grid over a 256 x 256 tile of int4 B, three LDS stages.  Measured on
+    // MI355X at M = N = 4096 (kernel trace, against the loop further down):
+    // K = 4096 60.6 against 61.1 us, K = 8192 107.5 against 111.2 us; for
+    // int2 B it gained nothing at K = 4096 and lost 4 us at K = 1024.
+    constexpr bool kPP = BM == 256 && BN == 256 && WAVES == 8 && WGM == 2 && STAGES == 3 && !NF4 && !SPLIT &&
+                         BITS == 4;
     static_assert(!NF4 || (BITS == 2 && F16OUT && !FUSE), "NF4: int2 byte layout, fp16 output, no fused epilogue");
     constexpr int kThreads = T::kThreads;
     static_assert(STAGES >= 2 && STAGES <= 8, "two to eight LDS stages");
@@ -468,7 +475,106 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             }
     }
 
-    if constexpr (!T::kAhead) {
+    if constexpr (kPP) {
+        // ---- ping-pong loop (256 x 256 tiles of packed B) ----
+        // The two wavefronts that share a SIMD (w and w + 4) take turns: while
+        // one runs a stage's matrix-core work from registers, the other issues
+        // its share of the loads two stages ahead and reads its operands of
+        // the stage from LDS.  Each phase ends at a workgroup barrier; group 1
+        // (waves 4-7) starts one phase late (an extra barrier at the start,
+        // matched by one at the end for group 0), so the groups stay in
+        // opposite phases and each SIMD's matrix core always has a wavefront
+        // feeding it.
+        //
+        // Phases are numbered by the barrier that ends them (barrier 0 ends
+        // the prologue).  Group 0 reads stage s in phase 2s+1 and computes it
+        // in 2s+2; group 1 reads it in 2s+2 and computes it in 2s+3.  Ring
+        // buffer (s+2) mod 3 last held stage s-1, read in phases 2s-1 and 2s,
+        // so the loads of stage s+2, issued in the reading phase of stage s
+        // (2s+1 or 2s+2), never overwrite data still to be read.  Stage s+1 is
+        // first read in phase 2s+3, so each wavefront's loads of it must have
+        // landed by barrier 2s+2: group 0 waits at the end of its compute
+        // phase 2s+2, group 1 at the end of its reading phase 2s+2, both with
+        // only their stage s+2 loads still allowed in flight.
+        constexpr int kPk = 4 / T::kSPR;  // packed B reads per stage
+        const int grp = wave >> 2;
+        v4i pa[4][T::kFM];
+        uint4 pb[kPk][T::kFN];
+        auto read_all = [&](int step) {
+            const int8_t *la = lds + (step % STAGES) * T::kStage;
+            const int8_t *lb = la + T::kSA;
+#pragma unroll
+            for (int q = 0; q < kPk; ++q) {
+                const int chunk = 2 * q + fg;
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j) {
+                    const int row = wn * T::kWN + j * 32 + fr;
+                    pb[q][j] = *(const uint4 *)(lb + row * T::kPB +
+                                                ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int chunk = (2 * (ks / T::kSPR) + fg) * T::kSPR + ks % T::kSPR;
+#pragma unroll
+                for (int i = 0; i < T::kFM; ++i) {
+                    const int row = wm * T::kWM + i * 32 + fr;
+                    pa[ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+                }
+            }
+        };
+        auto unpack_pp = [&](int ks, int slot) {
+#pragma unroll
+            for (int j = 0; j < T::kFN; ++j)
+                bop[slot][j] = U::operand_rt(pb[ks / T::kSPR][j], ks % T::kSPR);
+        };
+        auto barrier = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        issue_stage(0, 0, 1);
+        issue_stage(1, 0, 1);
+        wait_vmcnt<T::kDma>();  // this wavefront's stage 0 loads
+        barrier();
+        if (grp == 1)
+            barrier();
+        for (int step = 0; step < steps; ++step) {
+            // reading phase
+            issue_stage(step + 2, 0, 1);
+            read_all(step);
+            if (grp == 1)
+                wait_vmcnt<T::kDma>();
+            wait_lgkmcnt<0>();
+            unpack_pp(0, 0);
+            barrier();
+            // compute phase: sub-step ks on the matrix cores while the B
+            // operands of ks+1 are unpacked
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j)
+#pragma unroll
+                    for (int i = 0; i < T::kFM; ++i)
+                        acc[i][j] = mma32<NF4>(bop[ks & 1][j], pa[ks][i], acc[i][j]);
+                if (ks < 3)
+                    unpack_pp(ks + 1, (ks + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < T::kFM * T::kFN; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (grp == 0)
+                wait_vmcnt<T::kDma>();
+            barrier();
+        }
+        if (grp == 0)
+            barrier();
+    } else if constexpr (!T::kAhead) {
     // ---- prologue: stages 0 .. STAGES-2 in flight, stage 0 landed ----
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)

@@ -251,8 +251,9 @@ def test_calib_library_exports(bq):
     if not os.path.exists(_build.CALIB_LIB):
         _build.build_calib()
     lib = ctypes.CDLL(_build.CALIB_LIB)
-    for name in ("bq_calib_mfma_loop", "bq_calib_read_stream"):
+    for name in ("bq_calib_mfma_loop", "bq_calib_mfma_w4a8_stream", "bq_calib_read_stream"):
         assert hasattr(lib, name), name
     # invalid arguments are rejected before any launch (no GPU needed)
     assert lib.bq_calib_mfma_loop(0, 1, None, None) != 0
+    assert lib.bq_calib_mfma_w4a8_stream(0, 1, None, None) != 0
     assert lib.bq_calib_read_stream(None, ctypes.c_int64(16), 1, None, None) != 0
