@@ -37,7 +37,7 @@
 //    instruction per sub-step) instead read a whole stage of operands one
 //    stage ahead.
 //  * Epilogue: fp16(acc * scale) rows are staged through LDS and written
-//    with 16-byte coalesced stores.
+//    with 16-byte coalesced streaming (nontemporal) stores.
 //  * With few output tiles and a workspace from the caller, K is split over
 //    several workgroups per tile; the last to finish adds the others'
 //    partial sums (SplitK below).
@@ -834,7 +834,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 if (m < M && n < N) {
                     void *dst = (int8_t *)C + ((int64_t)m * N + n) * T::kES;
                     if (vecN && n + kPerChunk <= N) {
-                        *(uint4 *)dst = v;
+                        // streaming store: the output is not read again by
+                        // this kernel, and lines marked so leave L2 early
+                        // instead of being written back at the kernel's end
+                        // (M = N = K = 4096: 57.7 against 59.0 us)
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), (v4i *)dst);
                     } else {
                         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
                         if constexpr (F16OUT) {
