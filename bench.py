@@ -2,15 +2,16 @@
 """Benchmark of the quantized-GEMM hot path on one MI355X.
 
 One step is one pass of every kernel of the path over one batch of
-synthetic, HBM-resident inputs, in the order a model would run them:
+synthetic, HBM-resident inputs: weight preparation and the decode-sized
+GEMMs first, the prefill GEMM last:
 
   1. quantize_rows   fp16 fused-QKV weight [12288, 4096] -> int8 codes + fp16 scales
   2. gemm w8a8       those codes, M = 64 (streaming matrix-core path)
   3. pack_int4       int4 weight values [4096, 4096] -> [4096, 2048] bytes
   4. gemm w4a8       decode GEMV, M = 1, N = K = 4096
-  5. gemm w4a8       prefill, M = 4096, N = K = 4096 (tiled matrix-core path)
-  6. pack_int2       ternary weight values [4096, 4096] -> [4096, 1024] bytes
-  7. gemm w2a8       ternary, M = 1 and M = 128, N = K = 4096
+  5. pack_int2       ternary weight values [4096, 4096] -> [4096, 1024] bytes
+  6. gemm w2a8       ternary, M = 1 and M = 128, N = K = 4096
+  7. gemm w4a8       prefill, M = 4096, N = K = 4096 (tiled matrix-core path)
 
 Memory-bound steps read their inputs from rings of distinct buffers larger
 than twice the 256 MB Infinity Cache, so every timed read comes from HBM.
@@ -904,8 +905,8 @@ def build_line(args, meas, trace, why):
         "timing": timing,
         "config": {
             "workload": "w4a8 dequant GEMM M=4096 N=4096 K=4096 within one pass of the path "
-                        "(quantize 12288x4096, w8a8 M=64, pack int4/int2, w4a8 M=1 and 4096, "
-                        "w2a8 M=1 and 128)",
+                        "(quantize 12288x4096, w8a8 M=64 N=12288, pack int4, w4a8 M=1, pack int2, "
+                        "w2a8 M=1 and 128, w4a8 M=4096)",
             "M": 4096, "N": 4096, "K": 4096, "weight_bits": 4,
         },
         "gemv_m1": {"us": gemv["us"], "GB_per_s": gemv["GB_per_s"], "frac_of_hbm_peak": gemv["frac_of_bound"],

@@ -224,8 +224,8 @@ int bq_gemm(const int8_t *A, const void *B, int bits, const void *scale_f16,
  * than 128 tiles of 64 x 64, or K is shorter than 1024), else 4096 bytes of
  * per-tile counters plus 16 KiB of partial sums for each of the (at most
  * 256) workgroups, at most 4 MiB + 4 KiB in all.  Negative: -BQ_ERR_ARG or
- * -BQ_ERR_SHAPE for
- * arguments bq_gemm would reject.  Host-only; no device call.
+ * -BQ_ERR_SHAPE for arguments bq_gemm would reject.  Host-only; no device
+ * call.
  */
 int64_t bq_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits);
 
