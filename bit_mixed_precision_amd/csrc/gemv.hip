@@ -178,18 +178,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
         scBits = scale[min(myN, N - 1)];
         xsBits = (xscale ? xscale : scale)[xscale ? min(myM, M - 1) : 0];
     }
-    // per-lane DMA offsets within a pass (the pass's offset goes in the
-    // scalar operand)
+    // A in LDS piece-major: 1 KB block u * kH + h holds the 16-byte piece h
+    // of chunks 64 u + i (i = 0 ... 63) at 16 i, so that the 64 lanes' reads
+    // of one piece are consecutive 16-byte words (free of bank conflicts; a
+    // chunk-major layout puts the lanes 32 or 64 bytes apart).  The DMA lane
+    // i of block (u, h) reads that piece of chunk 64 u + i; the pass's offset
+    // goes in the scalar operand.
+    constexpr int kH = kAPerChunk / 16;  // 16-byte pieces of A per chunk
     uint32_t dmaOff[kAPass / 1024];
 #pragma unroll
-    for (int d = 0; d < kAPass / 1024; ++d)
-        dmaOff[d] = 1024u * d + 16u * lane;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+            dmaOff[u * kH + h] = (uint32_t)(64 * u + lane) * kAPerChunk + 16u * h;
 
     for (int c0 = 0, pass = 0; c0 < chunks; c0 += 64 * U, ++pass) {
         uint8_t(*as)[kAPass] = As[pass & 1];
-        // A of this pass into LDS: wavefront 0, coalesced 1 KB DMA blocks
-        // (k past K reads as zeros); issued before its B loads, so that its
-        // wait for the B loads' count leaves only them in flight
+        // A of this pass into LDS: wavefront 0, 1 KB DMA blocks (k past K
+        // reads as zeros); issued before its B loads, so that its wait for
+        // the B loads' count leaves only them in flight
         if (wave == 0) {
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
@@ -222,8 +229,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
 #pragma unroll
             for (int m = 0; m < MR; ++m)
 #pragma unroll
-                for (int h = 0; h < kAPerChunk / 16; ++h)
-                    a[m][h] = m < M ? *(const uint4 *)&as[m][(lane + 64 * u) * kAPerChunk + 16 * h]
+                for (int h = 0; h < kH; ++h)
+                    a[m][h] = m < M ? *(const uint4 *)&as[m][1024 * (u * kH + h) + 16 * lane]
                                     : make_uint4(0, 0, 0, 0);
             // the A bytes of the chunk in the order the packed B bytes unpack
             // in (once per chunk, shared by the wavefront's R rows)

@@ -186,6 +186,21 @@ def test_largest_tile_configuration(dev, bits, M, N, K):
     _check(acc, C, A, Bv, s, rows=rows, cols=cols, what=f"w{bits} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 8192), (4352, 4160, 4160)])
+def test_pingpong_loop_int4(dev, M, N, K):
+    """The 256 x 256 int4 tiles' ping-pong K loop: 64 stages, and 33 stages
+    ending in half a stage (K = 4160) with ragged last tile rows and
+    columns (17 x 17 tiles); int32 and fp16 outputs on sampled rows and
+    columns, the last ones included."""
+    banner(f"gemm pingpong int4 M={M} N={N} K={K}")
+    A, Bv, Bp, s = _make(4, M, N, K, seed=M + N + K)
+    acc, C = _run(dev, 4, A, Bp, s, "auto")
+    g = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([g.choice(M, 48, replace=False), np.arange(M - 4, M), [0, 255, 256]]))
+    cols = np.unique(np.concatenate([g.choice(N, 512, replace=False), np.arange(N - 70, N), [0, 255, 256]]))
+    _check(acc, C, A, Bv, s, rows=rows, cols=cols, what=f"w4 pingpong {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("bits", [8, 4, 2])
 @pytest.mark.parametrize("path", ["gemv", "stream", "tiled"])
 def test_k_zero_and_empty(dev, bits, path):
