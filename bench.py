@@ -61,9 +61,9 @@ STEP_NAMES = ["quantize_rows", "gemm_w8a8_m64", "pack_int4", "gemm_w4a8_m1",
               "pack_int2", "gemm_w2a8_m1", "gemm_w2a8_m128", "gemm_w4a8_m4096"]
 # same-size cold reads beside the decode GEMVs (algorithmic bytes of W2A8 and
 # W4A8 at M = 1, N = K = 4096, and W4A8 at N = 11008)
+READ_SIZES = {"gemm_w2a8_m1": 4214784, "gemm_w4a8_m1": 8409088, "gemm_w4a8_m1_n11008": 22592512}
 # iterations of the W4A8-data matrix-core loop (32 instructions each)
 STREAM_ITERS = 500
-READ_SIZES = {"gemm_w2a8_m1": 4214784, "gemm_w4a8_m1": 8409088, "gemm_w4a8_m1_n11008": 22592512}
 
 
 def parse(argv=None):

@@ -167,11 +167,19 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_stream_kernel(
         bK[d] = 16 * lc * 8 / BITS;
     }
     const int nch = (K + kKC - 1) / kKC;
+    // For int8 B the chunk order is rotated by the tile's column block, so
+    // that the workgroups streaming different B rows at the same time are at
+    // different k, while the M tiles of one column block stay together and
+    // share B in their XCD's L2 (W8A8 M = 64, N = 12288: 16.5 -> 15.2 us with
+    // 64 x 64 tiles, 14.5 -> 13.6 with 64 x 48).  For int4 / int2 B at
+    // N = K = 4096 the rotation cost 1-6 %, so they keep the plain order.  The
+    // sums do not depend on the order.
+    const int rot = (BITS == 8 && nch > 0) ? (tn * 3) % nch : 0;
     // DMA of chunk c into buffer b (zeros for k past K: each 16 bytes of a
     // row is wholly below or above K, a multiple of 64)
     auto issue = [&](int c, int b) {
         const uint32_t base = wlAddr + b * kBuf;
-        const int k0 = c * kKC;
+        const int k0 = (c + rot < nch ? c + rot : c + rot - nch) * kKC;
 #pragma unroll
         for (int d = 0; d < kDmaA; ++d)
             dma16(rA, base + 1024 * d, k0 + aK[d] < K ? aOff[d] + (uint32_t)k0 : kOOB, 0);
@@ -370,29 +378,42 @@ hipError_t launch_cfg(int idx, const int8_t *A, const uint8_t *B, const uint16_t
 // bytes at the per-CU rate (about 75 GB/s measured, LDS-DMA into a
 // workgroup's buffers), while B, N K bits/8 bytes, leaves HBM once (about
 // 5.5 TB/s); the estimate is the larger of the two, the two rates entering
-// as their ratio, with padded outputs as a tie-break.
+// as their ratio, with padded outputs as a tie-break, then the squarer tile
+// (32 x 32 over 16 x 64: 6.1 against 6.5 us at M = 64, N = K = 4096, int4
+// and int2).  When the winner runs in one round of workgroups, a tiling of
+// the same height that ties with it and keeps more CUs busy in one round
+// is taken instead (W8A8 M = 64, N = 12288: 64 x 48 on all 256 CUs 14.5 us,
+// 64 x 64 on 192 CUs 15.7 us; both bound by the same HBM bytes).
 int choose_cfg(int M, int N, int bits, int batch)
 {
     constexpr int64_t kCUs = 256;
     constexpr int64_t kHbmOverCu = 73;  // HBM rate / per-CU operand rate (5.5 TB/s / 75 GB/s)
+    int64_t main[kNumCfgs], tiles[kNumCfgs];
     int best = 0;
     int64_t bestCost = INT64_MAX;
     for (int c = 0; c < kNumCfgs; ++c) {
         const Cfg &g = kCfgs[c];
-        const int64_t tiles = (int64_t)((M + g.tm - 1) / g.tm) * ((N + g.tn - 1) / g.tn) * batch;
-        const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+        tiles[c] = (int64_t)((M + g.tm - 1) / g.tm) * ((N + g.tn - 1) / g.tn) * batch;
+        const int64_t rounds = (tiles[c] + kCUs - 1) / kCUs;
         // per-K byte counts, times 8 to keep the int2 quarter byte integral
         const int64_t perCu = rounds * (8 * g.tm + g.tn * bits);
         const int64_t hbm = (int64_t)N * bits * batch / kHbmOverCu;
-        const int64_t waste = tiles * g.tm * g.tn - (int64_t)M * N * batch;  // padded outputs
-        // ties go to the squarer tile (32 x 32 over 16 x 64: 6.1 against
-        // 6.5 us at M = 64, N = K = 4096, int4 and int2)
+        const int64_t waste = tiles[c] * g.tm * g.tn - (int64_t)M * N * batch;  // padded outputs
+        main[c] = (perCu > hbm ? perCu : hbm) * 64 + waste / 64;
         const int64_t skew = g.tm > g.tn ? g.tm - g.tn : g.tn - g.tm;
-        const int64_t cost = ((perCu > hbm ? perCu : hbm) * 64 + waste / 64) * 64 + skew;
+        const int64_t cost = main[c] * 64 + skew;
         if (cost < bestCost) {
             bestCost = cost;
             best = c;
         }
+    }
+    if (tiles[best] <= kCUs) {
+        int pick = best;
+        for (int c = 0; c < kNumCfgs; ++c)
+            if (kCfgs[c].tm == kCfgs[best].tm && main[c] == main[best] && tiles[c] <= kCUs &&
+                tiles[c] > tiles[pick])
+                pick = c;
+        best = pick;
     }
     return best;
 }
