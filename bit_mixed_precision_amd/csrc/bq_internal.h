@@ -42,11 +42,11 @@ hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStr
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 
 // erfc in fp32 for the GELU epilogue: exp(-x^2) * P(t), t = 1 / (1 + 0.4|x|),
-// with P the degree-8 fit of exp(x^2) erfc(x) on [0, 4.5] from
-// gen_erfc_fit.py (relative error about 6e-9 in double; with the fp32
+// with P the degree-6 fit of exp(x^2) erfc(x) on [0, 4.5] from
+// gen_erfc_fit.py (relative error about 3e-7 in double; with the fp32
 // arithmetic here about 2e-6, far below half an fp16 ulp), erfc(-x) =
 // 2 - erfc(x); |x| is clamped to 4.5, past which GELU's value is far below
-// half the smallest fp16 subnormal.  About 15 VALU operations.
+// half the smallest fp16 subnormal.  About 13 VALU operations.
 __device__ __forceinline__ float erfc_fit(float x)
 {
     const float ax = fminf(fabsf(x), kErfcFitXmax);
@@ -87,8 +87,8 @@ struct BatchStrides {
 // Decode GEMV on the dot-product ALUs, M <= 4.
 hipError_t launch_gemv(const int8_t *A, const uint8_t *B, int bits, const uint16_t *scale,
                        const uint16_t *xscale, int act, void *C, int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
-// Streaming matrix-core GEMM (operands straight into registers, K split over
-// the wavefronts of a workgroup), M <= 256.
+// Streaming matrix-core GEMM (operands through per-wavefront LDS-DMA chunk
+// buffers, K split over the wavefronts of a workgroup), M <= 256.
 hipError_t launch_gemm_stream(const int8_t *A, const uint8_t *B, int bits,
                               const uint16_t *scale, const uint16_t *xscale, int act, void *C,
                               int M, int N, int K, int batch, const BatchStrides &bs, hipStream_t s);
