@@ -90,7 +90,7 @@ def parse(argv=None):
 # Kernel sources of the tiled matrix-core GEMM; the committed HBM-traffic
 # summary is used only while their code (comments and blank space aside) and
 # the compiler flags are unchanged.
-TILED_SOURCES = ["gemm_tiled.hip", "lds_dma.h", "unpack.h", "bq_internal.h", "nf4_decode.h", "nf4_table.h", "erfc_fit.h"]
+TILED_SOURCES = ["gemm_tiled.hip", "lds_dma.h", "unpack.h", "bq_internal.h", "nf4_decode.h", "nf4_table.h", "gelu_fit.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a8_m4096_hbm_traffic.txt")
 
 

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "erfc_fit.h"
+#include "gelu_fit.h"
 
 namespace bq {
 
@@ -41,35 +41,40 @@ hipError_t launch_quantize_pack(const uint16_t *x, int64_t rows, int64_t cols, i
 hipError_t launch_pack_int4(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_int2(const int8_t *v, int64_t total, uint8_t *out, hipStream_t s);
 
-// erfc in fp32 for the GELU epilogue: exp(-x^2) * P(t), t = 1 / (1 + 0.4|x|),
-// with P the degree-6 fit of exp(x^2) erfc(x) on [0, 4.5] from
-// gen_erfc_fit.py (relative error about 3e-7 in double; with the fp32
-// arithmetic here about 2e-6, far below half an fp16 ulp), erfc(-x) =
-// 2 - erfc(x); |x| is clamped to 4.5, past which GELU's value is far below
-// half the smallest fp16 subnormal.  About 13 VALU operations.
-__device__ __forceinline__ float erfc_fit(float x)
+// GELU(v) = v * Phi(v) in fp32 with the constants of gelu_fit.h (from
+// gen_gelu_fit.py): Phi(v) = 1 - H for v >= 0 and H for v < 0, where
+// H = erfc(|v| / sqrt 2) / 2 = exp2(v^2 kGeluE) Q(t), t = 1 / (1 + kGeluA |v|),
+// Q a degree-4 fit (relative error about 6e-5, eight times below the
+// smallest relative fp16 ulp); |v| is clamped to kGeluVmax inside t only.
+// About 11 VALU operations and two transcendental ones (rcp, exp2).
+__device__ __forceinline__ float gelu_fit(float v)
 {
-    const float ax = fminf(fabsf(x), kErfcFitXmax);
-    const float t = __builtin_amdgcn_rcpf(1.0f + kErfcFitP * ax);
-    float p = kErfcFitC[kErfcFitDeg];
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluA, fminf(fabsf(v), kGeluVmax), 1.0f));
+    float q = kGeluQ[kGeluDeg];
 #pragma unroll
-    for (int k = kErfcFitDeg - 1; k >= 0; --k)
-        p = __builtin_fmaf(p, t, kErfcFitC[k]);
-    const float e = __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
-    const float E = e * p;
-    return x >= 0.0f ? E : 2.0f - E;
+    for (int k = kGeluDeg - 1; k >= 0; --k)
+        q = __builtin_fmaf(q, t, kGeluQ[k]);
+    const float h = __builtin_amdgcn_exp2f(v * v * kGeluE) * q;
+    return v * (v >= 0.0f ? 1.0f - h : h);
 }
 
 // Activation applied to the dequantized fp32 value before the fp16
-// conversion: 0 identity, 1 ReLU, 2 GELU v * Phi(v) with the standard normal
-// CDF Phi(v) = erfc(-v / sqrt(2)) / 2 (no cancellation for negative v).
+// conversion: 0 identity, 1 ReLU, 2 GELU (gelu_fit).  ACT fixed at compile
+// time (the tiled GEMM's epilogue), or chosen per call (apply_act).
+template <int ACT>
+__device__ __forceinline__ float act_fixed(float v)
+{
+    if constexpr (ACT == 1)
+        return fmaxf(v, 0.0f);
+    else if constexpr (ACT == 2)
+        return gelu_fit(v);
+    else
+        return v;
+}
+
 __device__ __forceinline__ float apply_act(float v, int act)
 {
-    if (act == 1)
-        return fmaxf(v, 0.0f);
-    if (act == 2)
-        return 0.5f * v * erfc_fit(-v * 0.70710678118654752f);
-    return v;
+    return act == 1 ? act_fixed<1>(v) : act == 2 ? act_fixed<2>(v) : v;
 }
 
 // Per-batch element strides of a batched GEMM launch (grid dimension y is the

@@ -35,9 +35,9 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, int *__restri
 
 // The matrix-core instruction stream of the W4A8 GEMM's 128-k stage with no
 // memory traffic: four 32-k sub-steps, each 2 B operands x 4 A operands into
-// 8 accumulators, on operands drawn like the workload's (A bytes uniform in
-// [-127, 127], B bytes 16 v with v uniform in [-8, 7], as the kernels feed
-// unpacked int4).  The matrix cores' power, and with it the clock they hold,
+// 8 accumulators, A operand first as in the GEMM, on operands drawn like the
+// workload's (A bytes uniform in [-127, 127], B bytes 16 v with v uniform in
+// [-8, 7], as the kernels feed unpacked int4).  The matrix cores' power, and with it the clock they hold,
 // depends on the operand bits; constant operands (mfma_loop_kernel) keep the
 // clock far higher than such data does.
 __global__ __launch_bounds__(256) void mfma_w4a8_stream_kernel(int iters, int *__restrict__ out)
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void mfma_w4a8_stream_kernel(int iters, int *_
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[ks][j], a[ks][i], c[i][j], 0, 0, 0);
+                    c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ks][i], b[ks][j], c[i][j], 0, 0, 0);
     }
     int s = 0;
 #pragma unroll

@@ -26,9 +26,13 @@
 //    permuted so that the DMA writes exactly this layout.
 //  * Wavefronts form a 2 x (WAVES/2) grid over the tile (1 x WAVES for
 //    some configurations, so that one wavefront unpacks each B column) and
-//    compute with v_mfma_i32_32x32x32_i8, B fragments as the first operand
-//    (so the accumulator holds C transposed: each lane owns 4 consecutive n
-//    of one row m), A fragments as the second.  Per 32-k sub-step a lane
+//    compute with v_mfma_i32_32x32x32_i8, A fragments as the first operand
+//    and B fragments as the second (each lane owns 4 consecutive rows m of
+//    one column n).  Under a sustained matrix-core load the clock is set by
+//    power, and this operand order draws less of it than the reverse with
+//    int8 activations against shifted int4 / int2 weights: M = N = K = 4096
+//    runs 4% (W4A8) and 7% (W2A8) faster, W8A8 and the fp16 NF4 mode the
+//    same.  Per 32-k sub-step a lane
 //    feeds 16 consecutive k of each operand; packed B is read 16 bytes at a
 //    time and unpacked in registers (unpack.h) into 1, 2 or 4 sub-steps.
 //  * Wave tiles of several fragments read the fragments of sub-step j+1
@@ -36,8 +40,9 @@
 //    the two halves of the last sub-step.  32 x 32 wave tiles (one matrix
 //    instruction per sub-step) instead read a whole stage of operands one
 //    stage ahead.
-//  * Epilogue: fp16(acc * scale) rows are staged through LDS and written
-//    with 16-byte coalesced streaming (nontemporal) stores.
+//  * Epilogue: fp16(acc * scale) values are staged through LDS (neighbouring
+//    lanes trade halves so that each LDS write holds two adjacent columns)
+//    and written as 16-byte coalesced streaming (nontemporal) stores.
 //  * With few output tiles and a workspace from the caller, K is split over
 //    several workgroups per tile; the last to finish adds the others'
 //    partial sums (SplitK below).
@@ -73,14 +78,14 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // One matrix-core step on a 32 x 32 tile: int8 x int8 -> int32 over 32 k,
-// or (NF4) fp16 x fp16 -> fp32 over 16 k; B fragment first (C transposed).
+// or (NF4) fp16 x fp16 -> fp32 over 16 k; A fragment first.
 template <bool NF4, typename Acc>
-__device__ __forceinline__ Acc mma32(const v4i &b, const v4i &a, const Acc &c)
+__device__ __forceinline__ Acc mma32(const v4i &a, const v4i &b, const Acc &c)
 {
     if constexpr (NF4)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, b), __builtin_bit_cast(v8h, a), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
 // Bit pattern of one accumulator element (taken by value: a bit cast of a
@@ -132,9 +137,10 @@ struct TiledCfg {
     static constexpr int kFN = kWN / 32;                // and N
     static constexpr int kSPR = 8 / BITS;               // sub-steps fed by one packed 16-byte read
     // epilogue staging: 64 rows (or fewer) of kWN outputs (fp16 or int32) per
-    // wave, rows padded by 16 bytes
+    // wave, rows padded by 32 bytes (bank offsets of the staging writes and
+    // copy-out reads below)
     static constexpr int kES = F16OUT ? 2 : 4;          // bytes per output element
-    static constexpr int kEpiPitch = kWN * kES + 16;
+    static constexpr int kEpiPitch = kWN * kES + 32;
     // 64 rows per pass, or 32 where 64 rows of every wave's tile would not fit in LDS
     static constexpr int kEpiRows = kWM < 64 ? kWM : WAVES * 64 * kEpiPitch <= 160 * 1024 ? 64 : 32;
     static constexpr int kEpiBytes = WAVES * kEpiRows * kEpiPitch;
@@ -370,47 +376,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                                         : U::template operand<3>(pk);
         }
     };
-    // matrix-core work of one sub-step on fragment rows [i0, i1), B-fragment
-    // major so the first instructions need only the first unpacked B operand
+    // matrix-core work of one sub-step on fragment rows [i0, i1), A-fragment
+    // major: each A operand stays in place for kFN consecutive instructions
+    // while the B operand changes, an order that draws less power than the
+    // reverse (M = N = K = 4096, power-limited: W2A8 3 %, W4A8 0.6 % faster)
     auto mfma_rows = [&](int oslot, int aslot, int i0, int i1) {
 #pragma unroll
-        for (int j = 0; j < T::kFN; ++j)
+        for (int i = i0; i < i1; ++i)
 #pragma unroll
-            for (int i = i0; i < i1; ++i)
-                acc[i][j] = mma32<NF4>(bop[oslot][j], fa[aslot][i], acc[i][j]);
+            for (int j = 0; j < T::kFN; ++j)
+                acc[i][j] = mma32<NF4>(fa[aslot][i], bop[oslot][j], acc[i][j]);
     };
     constexpr int kHalf = T::kFM / 2;
     constexpr int kReads = T::kFM + T::kFN;
 
-    // The lane's 4 x kFN groups of 4 consecutive scales for the fp16
-    // epilogue, loaded before the K loop so their latency is hidden by it.
-    uint2 sc[(F16OUT && !NF4) ? T::kFN : 1][4];
-    // with FUSE, the activation scale of each of the lane's kFM rows
-    float xsv[FUSE ? T::kFM : 1];
-    if constexpr (FUSE) {
-#pragma unroll
-        for (int i = 0; i < T::kFM; ++i) {
-            const int m = m0 + wm * T::kWM + i * 32 + fr;
-            xsv[i] = !xscale ? 1.0f : m < M ? __half2float(__ushort_as_half(xscale[m])) : 0.0f;
-        }
-    }
+    // The weight scale of the lane's column in each of its kFN fragments for
+    // the fp16 epilogue (fp32, with the exact int4 / int2 rescaling by
+    // 2^-kShift folded in), loaded before the K loop so that its latency is
+    // hidden by it.
+    float sc[(F16OUT && !NF4) ? T::kFN : 1];
     if constexpr (F16OUT && !NF4) {
-        const bool vecS = (N % 8) == 0;
+        constexpr float kInv = 1.0f / (float)(1 << U::kShift);
 #pragma unroll
-        for (int j = 0; j < T::kFN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * T::kWN + j * 32 + 8 * g + 4 * fg;
-                if (vecS && n + 4 <= N) {
-                    sc[j][g] = *(const uint2 *)(scale + n);
-                } else {
-                    uint32_t h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        h[e] = (n + e < N) ? scale[n + e] : 0u;
-                    sc[j][g] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                }
-            }
+        for (int j = 0; j < T::kFN; ++j) {
+            const int n = n0 + wn * T::kWN + j * 32 + fr;
+            sc[j] = n < N ? __half2float(__ushort_as_half(scale[n])) * kInv : 0.0f;
+        }
     }
 
     if constexpr (kPP) {
@@ -493,10 +484,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-                for (int j = 0; j < T::kFN; ++j)
+                for (int i = 0; i < T::kFM; ++i)
 #pragma unroll
-                    for (int i = 0; i < T::kFM; ++i)
-                        acc[i][j] = mma32<NF4>(bop[ks & 1][j], pa[ks][i], acc[i][j]);
+                    for (int j = 0; j < T::kFN; ++j)
+                        acc[i][j] = mma32<NF4>(pa[ks][i], bop[ks & 1][j], acc[i][j]);
                 if (ks < 3)
                     unpack_pp(ks + 1, (ks + 1) & 1);
 #pragma unroll
@@ -619,7 +610,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 for (int j = 0; j < T::kFN; ++j)
 #pragma unroll
                     for (int i = 0; i < T::kFM; ++i)
-                        acc[i][j] = mma32<NF4>(bo[j], ga[slot][u][ks][i], acc[i][j]);
+                        acc[i][j] = mma32<NF4>(ga[slot][u][ks][i], bo[j], acc[i][j]);
             }
         };
         // One step (stages step .. step+SPS-1): stages step+SPS ..
@@ -753,9 +744,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     }
 
     // ---- epilogue ----
-    // Accumulator layout (C transposed): lane l of acc[i][j] holds row
-    // m = wm*kWM + 32 i + (l & 31) and, in registers 4g..4g+3, the four
-    // consecutive columns n = wn*kWN + 32 j + 8 g + 4 (l >> 5) + (0..3).
+    // Accumulator layout: lane l of acc[i][j] holds column
+    // n = wn*kWN + 32 j + (l & 31) and, in registers 4g..4g+3, the four
+    // consecutive rows m = wm*kWM + 32 i + 8 g + 4 (l >> 5) + (0..3).
     // Both output types are staged through LDS, 64 rows (or fewer) of each
     // wave's tile at a time, and written as whole 16-byte chunks of rows.
     {
@@ -766,97 +757,144 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         constexpr int kChunksPerRow = T::kWN / kPerChunk;  // 16-byte chunks per staged row
         constexpr int kRowsPerIt = 64 / kChunksPerRow;
         constexpr int kFragsPerPass = T::kEpiRows / 32;
-        static_assert(kChunksPerRow <= 64 && 64 % kChunksPerRow == 0 && T::kEpiRows % kRowsPerIt == 0,
+        static_assert(kChunksPerRow <= 16 && 16 % kChunksPerRow == 0 && T::kEpiRows % kRowsPerIt == 0,
                       "epilogue copy-out shape");
+        // Copy-out: each 16 lanes read 16 / kChunksPerRow whole rows, spaced by
+        // kRowGap so that, with the 32-byte row padding, their 16-byte chunks
+        // fall in 16 distinct 16-byte bank groups.
+        constexpr int kRowsPer16 = 16 / kChunksPerRow;
+        constexpr int kRowGap = kRowsPer16 == 4 ? 2 : kRowsPer16 == 2 ? 4 : 1;
+        const int q16 = lane >> 4;
+        const int outRow = (q16 / kRowGap) * (kRowGap * kRowsPer16) + q16 % kRowGap +
+                           kRowGap * ((lane & 15) / kChunksPerRow);
+        const int outChunk = lane % kChunksPerRow;
+        const bool oddLane = (lane & 1) != 0;
+        // the passes, with the activation fixed at compile time (a per-element
+        // choice would keep the compiler from interleaving the elements'
+        // dependent chains)
+        auto passes = [&](auto actTag) {
+            constexpr int kAct = decltype(actTag)::value;
 #pragma unroll
-        for (int i0 = 0; i0 < T::kFM; i0 += kFragsPerPass) {
+            for (int i0 = 0; i0 < T::kFM; i0 += kFragsPerPass) {
+                // with FUSE, the activation scales of the lane's rows of this pass
+                // (four consecutive rows per 8-byte load: m is a multiple of 4)
+                float xs[FUSE ? kFragsPerPass : 1][4][4];
+                if constexpr (FUSE) {
 #pragma unroll
-            for (int j = 0; j < T::kFN; ++j) {
+                    for (int ii = 0; ii < kFragsPerPass; ++ii)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int nl = j * 32 + 8 * g + 4 * fg;  // first of 4 columns, wave-local
-                    if constexpr (F16OUT) {
-                        // scale / 2^kShift folds the exact int4/int2 rescaling into
-                        // the multiply (a power-of-two factor, exact in fp32)
-                        constexpr float kInv = 1.0f / (float)(1 << U::kShift);
-                        float s[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // NF4: the scale is in the weights
-                        if constexpr (!NF4) {
-                            s[0] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x & 0xFFFF))) * kInv;
-                            s[1] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].x >> 16))) * kInv;
-                            s[2] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y & 0xFFFF))) * kInv;
-                            s[3] = __half2float(__ushort_as_half((unsigned short)(sc[j][g].y >> 16))) * kInv;
-                        }
+                        for (int g = 0; g < 4; ++g) {
+                            const int m = m0 + wm * T::kWM + (i0 + ii) * 32 + 8 * g + 4 * fg;
+                            uint32_t h[4] = {0x3C00u, 0x3C00u, 0x3C00u, 0x3C00u};  // fp16 1.0 without xscale
+                            if (xscale) {
+                                if (m + 4 <= M) {
+                                    const uint2 p = *(const uint2 *)(xscale + m);
+                                    h[0] = p.x & 0xFFFF; h[1] = p.x >> 16; h[2] = p.y & 0xFFFF; h[3] = p.y >> 16;
+                                } else {
 #pragma unroll
-                        for (int ii = 0; ii < kFragsPerPass; ++ii) {
-                            const int i = i0 + ii;
-                            // weight scale, times the row's activation scale with
-                            // FUSE (a product of two fp16 values, exact in fp32),
-                            // then the activation
-                            float v[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                if constexpr (NF4)
-                                    v[e] = acc[i][j][4 * g + e];
-                                else
-                                    v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? s[e] * xsv[i] : s[e]);
-                                if constexpr (FUSE)
-                                    v[e] = apply_act(v[e], act);
+                                    for (int e = 0; e < 4; ++e)
+                                        h[e] = m + e < M ? xscale[m + e] : 0u;
+                                }
                             }
-                            // pairs converted as two-element fp16 vectors
-                            const h2v p01 = {(_Float16)v[0], (_Float16)v[1]};
-                            const h2v p23 = {(_Float16)v[2], (_Float16)v[3]};
-                            const int r = ii * 32 + fr;
-                            *(uint2 *)(stg + r * T::kEpiPitch + nl * 2) =
-                                make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
-                        }
-                    } else {
-                        // exact: the sums are multiples of 2^kShift
-#pragma unroll
-                        for (int ii = 0; ii < kFragsPerPass; ++ii) {
-                            const int i = i0 + ii;
-                            const int r = ii * 32 + fr;
-                            *(int4 *)(stg + r * T::kEpiPitch + nl * 4) =
-                                make_int4(acc[i][j][4 * g] >> U::kShift, acc[i][j][4 * g + 1] >> U::kShift,
-                                          acc[i][j][4 * g + 2] >> U::kShift, acc[i][j][4 * g + 3] >> U::kShift);
-                        }
-                    }
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int it = 0; it < T::kEpiRows / kRowsPerIt; ++it) {
-                const int r = it * kRowsPerIt + lane / kChunksPerRow;
-                const int c = lane % kChunksPerRow;
-                const uint4 v = *(const uint4 *)(stg + r * T::kEpiPitch + c * 16);
-                const int m = m0 + wm * T::kWM + i0 * 32 + r;
-                const int n = n0 + wn * T::kWN + c * kPerChunk;
-                if (m < M && n < N) {
-                    void *dst = (int8_t *)C + ((int64_t)m * N + n) * T::kES;
-                    if (vecN && n + kPerChunk <= N) {
-                        // streaming store: the output is not read again by
-                        // this kernel, and lines marked so leave L2 early
-                        // instead of being written back at the kernel's end
-                        // (M = N = K = 4096: 57.7 against 59.0 us)
-                        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), (v4i *)dst);
-                    } else {
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                        if constexpr (F16OUT) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                if (n + e < N)
-                                    ((uint16_t *)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                        } else {
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                if (n + e < N)
-                                    ((uint32_t *)dst)[e] = w[e];
+                                xs[ii][g][e] = __half2float(__ushort_as_half((unsigned short)h[e]));
+                        }
+                }
+#pragma unroll
+                for (int j = 0; j < T::kFN; ++j) {
+                    const int nl = j * 32 + fr;  // the lane's column, wave-local
+#pragma unroll
+                    for (int ii = 0; ii < kFragsPerPass; ++ii) {
+                        const int i = i0 + ii;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int r = ii * 32 + 8 * g + 4 * fg;  // first of the 4 rows, pass-local
+                            if constexpr (F16OUT) {
+                                // weight scale, times the row's activation scale with
+                                // FUSE (a product of two fp16 values, exact in fp32),
+                                // then the activation
+                                float v[4];
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    if constexpr (NF4)
+                                        v[e] = acc[i][j][4 * g + e];  // the scale is in the weights
+                                    else
+                                        v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? sc[j] * xs[ii][g][e] : sc[j]);
+                                    v[e] = act_fixed<kAct>(v[e]);
+                                }
+                                // rows (r, r+1) and (r+2, r+3) of column nl as fp16 pairs;
+                                // the even lane of each pair of columns keeps rows r, r+1
+                                // and takes those of its odd neighbour, which keeps
+                                // rows r+2, r+3, so each LDS write is two adjacent
+                                // columns of one row (DPP quad_perm [1,0,3,2]: lane ^ 1)
+                                const h2v p01 = {(_Float16)v[0], (_Float16)v[1]};
+                                const h2v p23 = {(_Float16)v[2], (_Float16)v[3]};
+                                const uint32_t x01 = __builtin_bit_cast(uint32_t, p01);
+                                const uint32_t x23 = __builtin_bit_cast(uint32_t, p23);
+                                const uint32_t keep = oddLane ? x23 : x01;
+                                const uint32_t got =
+                                    (uint32_t)__builtin_amdgcn_mov_dpp((int)(oddLane ? x01 : x23), 0xB1, 0xF, 0xF, false);
+                                const uint32_t lo = oddLane ? got : keep;   // the even column
+                                const uint32_t hi = oddLane ? keep : got;   // the odd column
+                                const int rr = r + (oddLane ? 2 : 0);
+                                int8_t *p = stg + rr * T::kEpiPitch + (nl & ~1) * 2;
+                                *(uint32_t *)p = (lo & 0xFFFFu) | (hi << 16);
+                                *(uint32_t *)(p + T::kEpiPitch) = (lo >> 16) | (hi & 0xFFFF0000u);
+                            } else {
+                                // exact: the sums are multiples of 2^kShift
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    *(int *)(stg + (r + e) * T::kEpiPitch + nl * 4) = acc[i][j][4 * g + e] >> U::kShift;
+                            }
                         }
                     }
                 }
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int it = 0; it < T::kEpiRows / kRowsPerIt; ++it) {
+                    const int r = it * kRowsPerIt + outRow;
+                    const uint4 v = *(const uint4 *)(stg + r * T::kEpiPitch + outChunk * 16);
+                    const int m = m0 + wm * T::kWM + i0 * 32 + r;
+                    const int n = n0 + wn * T::kWN + outChunk * kPerChunk;
+                    if (m < M && n < N) {
+                        void *dst = (int8_t *)C + ((int64_t)m * N + n) * T::kES;
+                        if (vecN && n + kPerChunk <= N) {
+                            // streaming store: the output is not read again by
+                            // this kernel, and lines marked so leave L2 early
+                            // instead of being written back at the kernel's end
+                            // (M = N = K = 4096: 57.7 against 59.0 us)
+                            __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), (v4i *)dst);
+                        } else {
+                            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                            if constexpr (F16OUT) {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e)
+                                    if (n + e < N)
+                                        ((uint16_t *)dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (n + e < N)
+                                        ((uint32_t *)dst)[e] = w[e];
+                            }
+                        }
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                __builtin_amdgcn_wave_barrier();
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_wave_barrier();
+        };
+        if constexpr (FUSE) {
+            if (act == 2)
+                passes(std::integral_constant<int, 2>{});
+            else if (act == 1)
+                passes(std::integral_constant<int, 1>{});
+            else
+                passes(std::integral_constant<int, 0>{});
+        } else {
+            passes(std::integral_constant<int, 0>{});
         }
     }
 }
