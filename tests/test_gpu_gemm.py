@@ -201,6 +201,35 @@ def test_pingpong_loop_int4(dev, M, N, K):
     _check(acc, C, A, Bv, s, rows=rows, cols=cols, what=f"w4 pingpong {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("K", [0, 64, 128, 256, 384])
+def test_pingpong_short_k(dev, K):
+    """The ping-pong loop with 0-3 stages of K (K = 64: one stage, half of it
+    past K), where its prologue's and last steps' loads past the end and its
+    group barriers meet: every column of 288 rows (each tile's first and last
+    rows among them), int32 and fp16, against the oracle; K = 0 gives zeros
+    everywhere."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    M = N = 4096
+    banner(f"gemm pingpong short K={K}")
+    if K == 0:
+        A = torch.zeros((M, 0), dtype=torch.int8, device=dev)
+        B = torch.zeros((N, 0), dtype=torch.uint8, device=dev)
+        s = torch.ones((N,), dtype=torch.float16, device=dev)
+        C = bq.gemm(A, B, 4, s, out=torch.full((M, N), 7.0, dtype=torch.float16, device=dev))
+        acc = bq.gemm(A, B, 4, None, out=torch.full((M, N), 7, dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+        assert not acc.cpu().numpy().any()
+        assert not f16_bits(C).any()
+        return
+    A, Bv, Bp, s = _make(4, M, N, K, seed=K + 11)
+    acc, C = _run(dev, 4, A, Bp, s, "auto")
+    g = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([g.choice(M, 256, replace=False), np.arange(0, M, 256), np.arange(255, M, 256)]))
+    _check(acc, C, A, Bv, s, rows=rows, what=f"w4 pingpong short K={K}")
+
+
 @pytest.mark.parametrize("bits", [8, 4, 2])
 @pytest.mark.parametrize("path", ["gemv", "stream", "tiled"])
 def test_k_zero_and_empty(dev, bits, path):
