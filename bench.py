@@ -410,6 +410,17 @@ def child(args):
         A_nf = up(g16.standard_normal((Mn, K)).astype(np.float16))
         C_nf = torch.empty((Mn, 4096), dtype=torch.float16, device=dev)
         timed(f"w4a16_nf4_m{Mn}", lambda i: bq.gemm_nf4_a16(A_nf, nf_ring[i % len(nf_ring)], s_nf, z_nf, out=C_nf))
+        if Mn == 4096 and R.mode == "measure":
+            # context: the vendor library's dense fp16 GEMM (torch.matmul, i.e.
+            # hipBLASLt, fp32 accumulation) on the same activations and the
+            # fp16 weights these codes decode to (the library's product with
+            # the identity gives them exactly): the matrix cores' clock depends
+            # on the values they multiply, so the comparison takes the same ones
+            eye = torch.eye(K, dtype=torch.float16, device=dev)
+            Wt = [bq.gemm_nf4_a16(eye, nf_ring[r], s_nf, z_nf) for r in range(2)]  # [K, N]: W[n, k] at [k, n]
+            del eye
+            timed("vendor_fp16_gemm_4096_nf4_values", lambda i: torch.matmul(A_nf, Wt[i % 2], out=C_nf))
+            del Wt
         del A_nf, C_nf
     del nf_ring, codes_nf
 
@@ -876,6 +887,13 @@ def build_line(args, meas, trace, why):
                                                     "us": v_us, "TOPS": round(ops / (v_us * 1e-6) / 1e12, 2)}
         ceilings["own_w8a8_i32_4096_events"] = {"us": o_us, "TOPS": round(ops / (o_us * 1e-6) / 1e12, 2),
                                                 "vs_vendor": round(v_us / o_us, 4)}
+    if "vendor_fp16_gemm_4096_nf4_values" in ev:
+        ops = roofline.gemm_ops(4096, 4096, K)
+        v_us, o_us = ev["vendor_fp16_gemm_4096_nf4_values"], ev["w4a16_nf4_m4096"]
+        ceilings["vendor_fp16_gemm_4096_nf4_values_events"] = {
+            "kernel": "torch.matmul (hipBLASLt), fp16 x fp16 -> fp16, the NF4 GEMM's activations and decoded weights",
+            "us": v_us, "TFLOPS": round(ops / (v_us * 1e-6) / 1e12, 2),
+            "own_nf4_us": o_us, "own_nf4_vs_vendor": round(v_us / o_us, 4)}
 
     cpu = meas.get("cpu_baseline")
     cfgs = meas.get("cpu_oracle_configs")
