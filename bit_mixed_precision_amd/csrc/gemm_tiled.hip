@@ -769,32 +769,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                            kRowGap * ((lane & 15) / kChunksPerRow);
         const int outChunk = lane % kChunksPerRow;
         const bool oddLane = (lane & 1) != 0;
-        // the passes, with the activation fixed at compile time (a per-element
-        // choice would keep the compiler from interleaving the elements'
-        // dependent chains)
-        auto passes = [&](auto actTag) {
+        // the passes, with the activation and the presence of token scales
+        // fixed at compile time (a per-element choice would keep the compiler
+        // from interleaving the elements' dependent chains)
+        auto passes = [&](auto actTag, auto xsTag) {
             constexpr int kAct = decltype(actTag)::value;
+            constexpr bool kXs = FUSE && decltype(xsTag)::value;
 #pragma unroll
             for (int i0 = 0; i0 < T::kFM; i0 += kFragsPerPass) {
-                // with FUSE, the activation scales of the lane's rows of this pass
+                // with token scales, those of the lane's rows of this pass
                 // (four consecutive rows per 8-byte load: m is a multiple of 4)
-                float xs[FUSE ? kFragsPerPass : 1][4][4];
-                if constexpr (FUSE) {
+                float xs[kXs ? kFragsPerPass : 1][4][4];
+                if constexpr (kXs) {
 #pragma unroll
                     for (int ii = 0; ii < kFragsPerPass; ++ii)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
                             const int m = m0 + wm * T::kWM + (i0 + ii) * 32 + 8 * g + 4 * fg;
-                            uint32_t h[4] = {0x3C00u, 0x3C00u, 0x3C00u, 0x3C00u};  // fp16 1.0 without xscale
-                            if (xscale) {
-                                if (m + 4 <= M) {
-                                    const uint2 p = *(const uint2 *)(xscale + m);
-                                    h[0] = p.x & 0xFFFF; h[1] = p.x >> 16; h[2] = p.y & 0xFFFF; h[3] = p.y >> 16;
-                                } else {
+                            uint32_t h[4];
+                            if (m + 4 <= M) {
+                                const uint2 p = *(const uint2 *)(xscale + m);
+                                h[0] = p.x & 0xFFFF; h[1] = p.x >> 16; h[2] = p.y & 0xFFFF; h[3] = p.y >> 16;
+                            } else {
 #pragma unroll
-                                    for (int e = 0; e < 4; ++e)
-                                        h[e] = m + e < M ? xscale[m + e] : 0u;
-                                }
+                                for (int e = 0; e < 4; ++e)
+                                    h[e] = m + e < M ? xscale[m + e] : 0u;
                             }
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
@@ -820,7 +819,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                                     if constexpr (NF4)
                                         v[e] = acc[i][j][4 * g + e];  // the scale is in the weights
                                     else
-                                        v[e] = (float)acc[i][j][4 * g + e] * (FUSE ? sc[j] * xs[ii][g][e] : sc[j]);
+                                        v[e] = (float)acc[i][j][4 * g + e] * (kXs ? sc[j] * xs[ii][g][e] : sc[j]);
                                     v[e] = act_fixed<kAct>(v[e]);
                                 }
                                 // rows (r, r+1) and (r+2, r+3) of column nl as fp16 pairs;
@@ -886,15 +885,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 __builtin_amdgcn_wave_barrier();
             }
         };
-        if constexpr (FUSE) {
+        auto with_act = [&](auto xsTag) {
             if (act == 2)
-                passes(std::integral_constant<int, 2>{});
+                passes(std::integral_constant<int, 2>{}, xsTag);
             else if (act == 1)
-                passes(std::integral_constant<int, 1>{});
+                passes(std::integral_constant<int, 1>{}, xsTag);
             else
-                passes(std::integral_constant<int, 0>{});
+                passes(std::integral_constant<int, 0>{}, xsTag);
+        };
+        if constexpr (FUSE) {
+            if (xscale)
+                with_act(std::true_type{});
+            else
+                with_act(std::false_type{});
         } else {
-            passes(std::integral_constant<int, 0>{});
+            passes(std::integral_constant<int, 0>{}, std::false_type{});
         }
     }
 }
