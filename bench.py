@@ -858,7 +858,9 @@ def build_line(args, meas, trace, why):
     loop_us = primary("mfma_i8_loop", ev.get("mfma_i8_loop"))[0]
     loop_tops = 1024 * 4 * 4000 * 4 * 65536 / (loop_us * 1e-6) / 1e12
     data_us = primary("mfma_i8_loop_w4a8_data", ev.get("mfma_i8_loop_w4a8_data"))[0]
-    data_tops = 1024 * 4 * STREAM_ITERS * 32 * 65536 / (data_us * 1e-6) / 1e12
+    # 2^21 operations per wavefront per iteration: one 128-k stage of the
+    # M = 4096 GEMM's wavefront (64 instructions of 16 x 16 x 64)
+    data_tops = 1024 * 4 * STREAM_ITERS * (1 << 21) / (data_us * 1e-6) / 1e12
     rd_us = primary("read_stream_1GiB", ev.get("read_stream_1GiB"))[0]
     rd_gbs = (1 << 30) / (rd_us * 1e-6) / 1e9
     ceilings = {

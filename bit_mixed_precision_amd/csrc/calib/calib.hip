@@ -34,12 +34,15 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, int *__restri
 }
 
 // The matrix-core instruction stream of the W4A8 GEMM's 128-k stage with no
-// memory traffic: four 32-k sub-steps, each 2 B operands x 4 A operands into
-// 8 accumulators, A operand first as in the GEMM, on operands drawn like the
-// workload's (A bytes uniform in [-127, 127], B bytes 16 v with v uniform in
-// [-8, 7], as the kernels feed unpacked int4).  The matrix cores' power, and with it the clock they hold,
-// depends on the operand bits; constant operands (mfma_loop_kernel) keep the
-// clock far higher than such data does.
+// memory traffic, as one wavefront of the M = 4096 kernel issues it: two 64-k
+// sub-steps of v_mfma_i32_16x16x64_i8, each 8 A operands x 4 B operands into
+// 32 accumulators, A first and each A operand held for four consecutive
+// instructions, on operands drawn like the workload's (A bytes uniform in
+// [-127, 127], B bytes 16 v with v uniform in [-8, 7], as the kernels feed
+// unpacked int4).  The matrix cores' power, and with it the clock they hold,
+// depends on the operand bits and on the instruction shape and order;
+// constant operands (mfma_loop_kernel) keep the clock far higher than such
+// data does.  2^21 operations per wavefront per iteration.
 __global__ __launch_bounds__(256) void mfma_w4a8_stream_kernel(int iters, int *__restrict__ out)
 {
     uint32_t h = (uint32_t)(blockIdx.x * blockDim.x + threadIdx.x) * 2654435761u + 0x9E3779B9u;
@@ -49,11 +52,11 @@ __global__ __launch_bounds__(256) void mfma_w4a8_stream_kernel(int iters, int *_
         h ^= h << 5;
         return h;
     };
-    v4i a[4][4], b[4][2];
+    v4i a[2][8], b[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 uint32_t w = 0;
@@ -63,28 +66,28 @@ __global__ __launch_bounds__(256) void mfma_w4a8_stream_kernel(int iters, int *_
                 a[ks][i][e] = (int)w;
             }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 b[ks][j][e] = (int)(next() & 0xF0F0F0F0u);
     }
-    v16i c[4][2] = {};
+    v4i c[8][4] = {};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ks][i], b[ks][j], c[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    c[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[ks][i], b[ks][j], c[i][j], 0, 0, 0);
     }
     int s = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
+            for (int e = 0; e < 4; ++e)
                 s ^= c[i][j][e];
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }

@@ -32,9 +32,11 @@
 //    power, and this operand order draws less of it than the reverse with
 //    int8 activations against shifted int4 / int2 weights: M = N = K = 4096
 //    runs 4% (W4A8) and 7% (W2A8) faster, W8A8 and the fp16 NF4 mode the
-//    same.  Per 32-k sub-step a lane
-//    feeds 16 consecutive k of each operand; packed B is read 16 bytes at a
-//    time and unpacked in registers (unpack.h) into 1, 2 or 4 sub-steps.
+//    same.  Per 32-k sub-step a lane feeds 16 consecutive k of each
+//    operand; packed B is read 16 bytes at a time and unpacked in registers
+//    (unpack.h) into 1, 2 or 4 sub-steps.  The 256 x 256 int4 ping-pong
+//    loop uses v_mfma_i32_16x16x64_i8 instead (16 x 16 fragments, two 64-k
+//    sub-steps per stage), which holds a higher clock for the same work.
 //  * Wave tiles of several fragments read the fragments of sub-step j+1
 //    while the matrix cores run j, with one barrier per stage placed between
 //    the two halves of the last sub-step.  32 x 32 wave tiles (one matrix
@@ -195,6 +197,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // int2 B it gained nothing at K = 4096 and lost 4 us at K = 1024.
     constexpr bool kPP = BM == 256 && BN == 256 && WAVES == 8 && WGM == 2 && STAGES == 3 && !NF4 && !SPLIT &&
                          BITS == 4;
+    // The ping-pong loop runs v_mfma_i32_16x16x64_i8 (16 x 16 output
+    // fragments), every other loop v_mfma_i32_32x32x32_i8 (32 x 32): under a
+    // sustained load the matrix cores hold a higher clock with the smaller
+    // instruction for the same work (a loop of the W4A8 GEMM's operands:
+    // 4.3-4.4 against 3.9 POP/s).
+    constexpr bool kM16 = kPP;
+    constexpr int kCF = kM16 ? 16 : 32;                      // output fragment edge
+    constexpr int kFMe = T::kWM / kCF, kFNe = T::kWN / kCF;  // fragments per wavefront
     static_assert(!NF4 || (BITS == 2 && F16OUT && !FUSE), "NF4: int2 byte layout, fp16 output, no fused epilogue");
     constexpr int kThreads = T::kThreads;
     static_assert(STAGES >= 2 && STAGES <= 8, "two to eight LDS stages");
@@ -336,12 +346,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     };
 
     using Acc = typename std::conditional<NF4, v16f, v16i>::type;
-    Acc acc[T::kFM][T::kFN];
+    using AccE = typename std::conditional<kM16, v4i, Acc>::type;
+    AccE acc[kFMe][kFNe];
 #pragma unroll
-    for (int i = 0; i < T::kFM; ++i)
+    for (int i = 0; i < kFMe; ++i)
 #pragma unroll
-        for (int j = 0; j < T::kFN; ++j)
-            acc[i][j] = (Acc){};
+        for (int j = 0; j < kFNe; ++j)
+            acc[i][j] = (AccE){};
 
     // NF4: the dequantized table of each B row this lane feeds (one per
     // fragment column j), in registers
@@ -381,11 +392,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // while the B operand changes, an order that draws less power than the
     // reverse (M = N = K = 4096, power-limited: W2A8 3 %, W4A8 0.6 % faster)
     auto mfma_rows = [&](int oslot, int aslot, int i0, int i1) {
+        if constexpr (!kM16) {
 #pragma unroll
-        for (int i = i0; i < i1; ++i)
+            for (int i = i0; i < i1; ++i)
 #pragma unroll
-            for (int j = 0; j < T::kFN; ++j)
-                acc[i][j] = mma32<NF4>(fa[aslot][i], bop[oslot][j], acc[i][j]);
+                for (int j = 0; j < T::kFN; ++j)
+                    acc[i][j] = mma32<NF4>(fa[aslot][i], bop[oslot][j], acc[i][j]);
+        }
     };
     constexpr int kHalf = T::kFM / 2;
     constexpr int kReads = T::kFM + T::kFN;
@@ -394,12 +407,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     // the fp16 epilogue (fp32, with the exact int4 / int2 rescaling by
     // 2^-kShift folded in), loaded before the K loop so that its latency is
     // hidden by it.
-    float sc[(F16OUT && !NF4) ? T::kFN : 1];
+    float sc[(F16OUT && !NF4) ? kFNe : 1];
     if constexpr (F16OUT && !NF4) {
         constexpr float kInv = 1.0f / (float)(1 << U::kShift);
 #pragma unroll
-        for (int j = 0; j < T::kFN; ++j) {
-            const int n = n0 + wn * T::kWN + j * 32 + fr;
+        for (int j = 0; j < kFNe; ++j) {
+            const int n = n0 + wn * T::kWN + j * kCF + (kM16 ? (lane & 15) : fr);
             sc[j] = n < N ? __half2float(__ushort_as_half(scale[n])) * kInv : 0.0f;
         }
     }
@@ -425,37 +438,47 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         // landed by barrier 2s+2: group 0 waits at the end of its compute
         // phase 2s+2, group 1 at the end of its reading phase 2s+2, both with
         // only their stage s+2 loads still allowed in flight.
-        constexpr int kPk = 4 / T::kSPR;  // packed B reads per stage
+        // 16 x 16 x 64 operands: lane l feeds row / column l & 15 of a
+        // fragment and, at 64-k sub-step s, the k [32 g + 16 s, +16) of its
+        // k group g = l >> 4 in both operands (the instruction sums over
+        // whatever k its lanes feed); a lane's 32 k of a stage's B row are
+        // one 16-byte packed read, unpacked into the two sub-steps' operands.
         const int grp = wave >> 2;
-        v4i pa[4][T::kFM];
-        uint4 pb[kPk][T::kFN];
+        const int l16 = lane & 15, g4 = lane >> 4;
+        v4i pa[2][kFMe];    // A operands of the stage's two sub-steps
+        uint4 pb[kFNe];     // packed B, 32 k per fragment column
+        v4i bq[2][kFNe];    // unpacked B operands, double buffered by sub-step
         auto read_all = [&](int step) {
             const int8_t *la = lds + (step % STAGES) * T::kStage;
             const int8_t *lb = la + T::kSA;
 #pragma unroll
-            for (int q = 0; q < kPk; ++q) {
-                const int chunk = 2 * q + fg;
-#pragma unroll
-                for (int j = 0; j < T::kFN; ++j) {
-                    const int row = wn * T::kWN + j * 32 + fr;
-                    pb[q][j] = *(const uint4 *)(lb + row * T::kPB +
-                                                ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
-                }
+            for (int j = 0; j < kFNe; ++j) {
+                const int row = wn * T::kWN + j * 16 + l16;
+                pb[j] = *(const uint4 *)(lb + row * T::kPB + ((g4 ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
             }
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int chunk = (2 * (ks / T::kSPR) + fg) * T::kSPR + ks % T::kSPR;
+            for (int st = 0; st < 2; ++st) {
+                const int chunk = 2 * g4 + st;
 #pragma unroll
-                for (int i = 0; i < T::kFM; ++i) {
-                    const int row = wm * T::kWM + i * 32 + fr;
-                    pa[ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+                for (int i = 0; i < kFMe; ++i) {
+                    const int row = wm * T::kWM + i * 16 + l16;
+                    pa[st][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
                 }
             }
         };
-        auto unpack_pp = [&](int ks, int slot) {
+        auto unpack_pp = [&](int st, int slot) {
 #pragma unroll
-            for (int j = 0; j < T::kFN; ++j)
-                bop[slot][j] = U::operand_rt(pb[ks / T::kSPR][j], ks % T::kSPR);
+            for (int j = 0; j < kFNe; ++j)
+                bq[slot][j] = U::operand_rt(pb[j], st);
+        };
+        // sub-step st's matrix work, A-fragment major (each A operand held
+        // for kFNe consecutive instructions)
+        auto mma_sub = [&](int st) {
+#pragma unroll
+            for (int i = 0; i < kFMe; ++i)
+#pragma unroll
+                for (int j = 0; j < kFNe; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[st][i], bq[st][j], acc[i][j], 0, 0, 0);
         };
         auto barrier = [&]() {
             __builtin_amdgcn_sched_barrier(0);
@@ -479,24 +502,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             wait_lgkmcnt<0>();
             unpack_pp(0, 0);
             barrier();
-            // compute phase: sub-step ks on the matrix cores while the B
-            // operands of ks+1 are unpacked
+            // compute phase: sub-step 0 on the matrix cores while the B
+            // operands of sub-step 1 are unpacked, then sub-step 1
+            mma_sub(0);
+            unpack_pp(1, 1);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int i = 0; i < T::kFM; ++i)
-#pragma unroll
-                    for (int j = 0; j < T::kFN; ++j)
-                        acc[i][j] = mma32<NF4>(pa[ks][i], bop[ks & 1][j], acc[i][j]);
-                if (ks < 3)
-                    unpack_pp(ks + 1, (ks + 1) & 1);
-#pragma unroll
-                for (int i = 0; i < T::kFM * T::kFN; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < kFMe * kFNe; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            mma_sub(1);
+            __builtin_amdgcn_sched_barrier(0);
             if (grp == 0)
                 wait_vmcnt<T::kDma>();
             barrier();
@@ -744,9 +761,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
     }
 
     // ---- epilogue ----
-    // Accumulator layout: lane l of acc[i][j] holds column
-    // n = wn*kWN + 32 j + (l & 31) and, in registers 4g..4g+3, the four
-    // consecutive rows m = wm*kWM + 32 i + 8 g + 4 (l >> 5) + (0..3).
+    // Accumulator layout: lane l of a 32 x 32 fragment acc[i][j] holds
+    // column n = wn*kWN + 32 j + (l & 31) and, in registers 4g..4g+3, the
+    // four consecutive rows m = wm*kWM + 32 i + 8 g + 4 (l >> 5) + (0..3); of
+    // a 16 x 16 fragment (the ping-pong loop), column wn*kWN + 16 j + (l & 15)
+    // and rows wm*kWM + 16 i + 4 (l >> 4) + (0..3): in both, groups of four
+    // consecutive rows of one column.
     // Both output types are staged through LDS, 64 rows (or fewer) of each
     // wave's tile at a time, and written as whole 16-byte chunks of rows.
     {
@@ -756,7 +776,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         int8_t *stg = lds + wave * T::kEpiRows * T::kEpiPitch;
         constexpr int kChunksPerRow = T::kWN / kPerChunk;  // 16-byte chunks per staged row
         constexpr int kRowsPerIt = 64 / kChunksPerRow;
-        constexpr int kFragsPerPass = T::kEpiRows / 32;
+        constexpr int kFragsPerPass = T::kEpiRows / kCF;
+        constexpr int kG = kM16 ? 1 : 4;  // groups of four rows per lane and fragment
+        static_assert(kG * 4 == (int)(sizeof(AccE) / 4), "a lane's accumulator holds kG groups of four rows");
+        // the first of a group's four rows, fragment-local
+        auto grow = [&](int g) { return kM16 ? 4 * (lane >> 4) : 8 * g + 4 * fg; };
+        const int fcol = kM16 ? (lane & 15) : fr;  // the lane's column, fragment-local
         static_assert(kChunksPerRow <= 16 && 16 % kChunksPerRow == 0 && T::kEpiRows % kRowsPerIt == 0,
                       "epilogue copy-out shape");
         // Copy-out: each 16 lanes read 16 / kChunksPerRow whole rows, spaced by
@@ -776,16 +801,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
             constexpr int kAct = decltype(actTag)::value;
             constexpr bool kXs = FUSE && decltype(xsTag)::value;
 #pragma unroll
-            for (int i0 = 0; i0 < T::kFM; i0 += kFragsPerPass) {
+            for (int i0 = 0; i0 < kFMe; i0 += kFragsPerPass) {
                 // with token scales, those of the lane's rows of this pass
                 // (four consecutive rows per 8-byte load: m is a multiple of 4)
-                float xs[kXs ? kFragsPerPass : 1][4][4];
+                float xs[kXs ? kFragsPerPass : 1][kG][4];
                 if constexpr (kXs) {
 #pragma unroll
                     for (int ii = 0; ii < kFragsPerPass; ++ii)
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int m = m0 + wm * T::kWM + (i0 + ii) * 32 + 8 * g + 4 * fg;
+                        for (int g = 0; g < kG; ++g) {
+                            const int m = m0 + wm * T::kWM + (i0 + ii) * kCF + grow(g);
                             uint32_t h[4];
                             if (m + 4 <= M) {
                                 const uint2 p = *(const uint2 *)(xscale + m);
@@ -801,14 +826,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                         }
                 }
 #pragma unroll
-                for (int j = 0; j < T::kFN; ++j) {
-                    const int nl = j * 32 + fr;  // the lane's column, wave-local
+                for (int j = 0; j < kFNe; ++j) {
+                    const int nl = j * kCF + fcol;  // the lane's column, wave-local
 #pragma unroll
                     for (int ii = 0; ii < kFragsPerPass; ++ii) {
                         const int i = i0 + ii;
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int r = ii * 32 + 8 * g + 4 * fg;  // first of the 4 rows, pass-local
+                        for (int g = 0; g < kG; ++g) {
+                            const int r = ii * kCF + grow(g);  // first of the 4 rows, pass-local
                             if constexpr (F16OUT) {
                                 // weight scale, times the row's activation scale with
                                 // FUSE (a product of two fp16 values, exact in fp32),
@@ -855,7 +880,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 for (int it = 0; it < T::kEpiRows / kRowsPerIt; ++it) {
                     const int r = it * kRowsPerIt + outRow;
                     const uint4 v = *(const uint4 *)(stg + r * T::kEpiPitch + outChunk * 16);
-                    const int m = m0 + wm * T::kWM + i0 * 32 + r;
+                    const int m = m0 + wm * T::kWM + i0 * kCF + r;
                     const int n = n0 + wn * T::kWN + outChunk * kPerChunk;
                     if (m < M && n < N) {
                         void *dst = (int8_t *)C + ((int64_t)m * N + n) * T::kES;
