@@ -75,6 +75,22 @@ constexpr int kSchedDsRead = 0x100;
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
+// 16-byte chunk permutation of an LDS row (XOR with a function of the row):
+// the DMA stores logical chunk c of row r at physical chunk c ^ swz(r), the
+// fragment reads undo it.  A ds_read_b128 is served 16 lanes per cycle from
+// 64 four-byte banks, the 16 lanes of one cycle being those with equal lane
+// bit 5 and equal parity of lane bits 2..4 (measured with bank-conflict
+// counters on lane pairs).  With s = the row's bits from `shift` up, the
+// plain s spreads the reads of 32-row fragments over all 64 banks in each
+// cycle, but puts the 16-row fragment reads of the 16x16x64 loop two to a
+// bank; s ^ (s << 1) (GRAY) serves both conflict-free.
+template <bool GRAY>
+__device__ __forceinline__ int swz(int row, int shift, int mask)
+{
+    const int s = row >> shift;
+    return (GRAY ? s ^ (s << 1) : s) & mask;
+}
+
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -122,6 +138,13 @@ struct TiledCfg {
     static constexpr int kCPR = kPB / 16;               // B 16-byte chunks per row
     static constexpr int kRowsPerLineB = 256 / kPB;     // B rows sharing a 256-byte bank line
     static constexpr int kSwzShiftB = ilog2(kRowsPerLineB);
+    // A rows use the GRAY chunk permutation on the 256 x 256 tiles: there it
+    // removes the 16x16x64 loop's bank conflicts and, on the 32 x 32 loops,
+    // measured faster with the same (zero) conflicts (M = N = K = 4096: W2A8
+    // 3.6 %, NF4 1.8 %, W8A8 even); on the 128 x 128 W4A8 tile it measured
+    // 4-9 % slower (M = 1024, 2048), so the smaller tiles keep the plain one.
+    // B rows keep the plain one: GRAY measured no faster on any tile.
+    static constexpr bool kGrayA = BM == 256 && BN == 256;
     static constexpr int kSA = BM * kBK;                // A bytes per stage
     static constexpr int kSB = BN * kPB;                // B bytes per stage
     static constexpr int kStage = kSA + kSB;
@@ -254,7 +277,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
     for (int p = 0; p < T::kDmaA; ++p) {
         const int row = (wave + WAVES * p) * 8 + aRowInBlk;
-        aChunkL[p] = (lane & 7) ^ ((row >> 1) & 7);
+        aChunkL[p] = (lane & 7) ^ swz<T::kGrayA>(row, 1, 7);
         aOff[p] = (uint32_t)row * (uint32_t)K + aChunkL[p] * 16;
     }
     // B block b (1024 / kPB rows): lane s -> row (1024/kPB) b + s / kCPR, chunk s % kCPR.
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
     for (int p = 0; p < T::kDmaB; ++p) {
         const int row = (wave + WAVES * p) * kBRowsPerBlk + lane / T::kCPR;
-        bChunkL[p] = (lane % T::kCPR) ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1));
+        bChunkL[p] = (lane % T::kCPR) ^ swz<false>(row, T::kSwzShiftB, T::kCPR - 1);
         bOff[p] = (uint32_t)row * rowBytesB + bChunkL[p] * 16;
     }
 
@@ -331,7 +354,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
         for (int i = 0; i < T::kFM; ++i) {
             const int row = wm * T::kWM + i * 32 + fr;
-            fa[slot][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+            fa[slot][i] = *(const v4i *)(la + row * kBK + ((chunk ^ swz<T::kGrayA>(row, 1, 7)) * 16));
         }
     };
     auto read_b = [&](int step, int q, int slot) {
@@ -341,7 +364,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         for (int j = 0; j < T::kFN; ++j) {
             const int row = wn * T::kWN + j * 32 + fr;
             fbp[slot][j] = *(const uint4 *)(lb + row * T::kPB +
-                                            ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+                                            ((chunk ^ swz<false>(row, T::kSwzShiftB, T::kCPR - 1)) * 16));
         }
     };
 
@@ -454,7 +477,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
             for (int j = 0; j < kFNe; ++j) {
                 const int row = wn * T::kWN + j * 16 + l16;
-                pb[j] = *(const uint4 *)(lb + row * T::kPB + ((g4 ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+                pb[j] = *(const uint4 *)(lb + row * T::kPB + ((g4 ^ swz<false>(row, T::kSwzShiftB, T::kCPR - 1)) * 16));
             }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -462,7 +485,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                 for (int i = 0; i < kFMe; ++i) {
                     const int row = wm * T::kWM + i * 16 + l16;
-                    pa[st][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+                    pa[st][i] = *(const v4i *)(la + row * kBK + ((chunk ^ swz<T::kGrayA>(row, 1, 7)) * 16));
                 }
             }
         };
@@ -598,7 +621,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
 #pragma unroll
                 for (int i = 0; i < T::kFM; ++i) {
                     const int row = wm * T::kWM + i * 32 + fr;
-                    ga[slot][u][ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ ((row >> 1) & 7)) * 16));
+                    ga[slot][u][ks][i] = *(const v4i *)(la + row * kBK + ((chunk ^ swz<T::kGrayA>(row, 1, 7)) * 16));
                 }
             }
 #pragma unroll
@@ -608,7 +631,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
                 for (int j = 0; j < T::kFN; ++j) {
                     const int row = wn * T::kWN + j * 32 + fr;
                     gb[slot][u][q][j] = *(const uint4 *)(lb + row * T::kPB +
-                                                         ((chunk ^ ((row >> T::kSwzShiftB) & (T::kCPR - 1))) * 16));
+                                                         ((chunk ^ swz<false>(row, T::kSwzShiftB, T::kCPR - 1)) * 16));
                 }
             }
         };
