@@ -58,14 +58,24 @@ __device__ __forceinline__ void fence()
 }
 
 // Chunk layout of one operand in LDS: rows of P bytes (the chunk's 128 k at
-// BITS bits), 16-byte pieces XOR-swizzled by the row bits above the rows
-// that share a 256-byte bank line.
+// BITS bits), 16-byte pieces XOR-swizzled by a function of the row bits
+// above the rows that share a 256-byte bank line.  A ds_read_b128 is served
+// 16 lanes per cycle from 64 four-byte banks, the lanes of one cycle being
+// those with equal lane bit 5 and equal parity of lane bits 2..4; the
+// fragment reads below take row 16 f + (lane & 15) and piece lane >> 4 (or
+// 2 (lane >> 4) + s), and with s = row / kL, s ^ (s << 1) puts the 16 lanes
+// of each cycle in 16 distinct bank groups (the plain s puts them two to a
+// group).
 template <int P>
 struct Rows {
     static constexpr int kQ = P / 16;          // 16-byte pieces per row
     static constexpr int kL = 256 / P;         // rows per 256-byte bank line
     static constexpr int kPerKB = 1024 / P;    // rows per 1 KB DMA instruction
-    __device__ __forceinline__ static int phys(int row, int piece) { return piece ^ ((row / kL) & (kQ - 1)); }
+    __device__ __forceinline__ static int phys(int row, int piece)
+    {
+        const int s = row / kL;
+        return piece ^ ((s ^ (s << 1)) & (kQ - 1));
+    }
 };
 
 // TM x TN output tile per workgroup; WN wavefronts split the tile's columns
