@@ -139,11 +139,12 @@ struct TiledCfg {
     static constexpr int kRowsPerLineB = 256 / kPB;     // B rows sharing a 256-byte bank line
     static constexpr int kSwzShiftB = ilog2(kRowsPerLineB);
     // A rows use the GRAY chunk permutation on the 256 x 256 tiles: there it
-    // removes the 16x16x64 loop's bank conflicts and, on the 32 x 32 loops,
-    // measured faster with the same (zero) conflicts (M = N = K = 4096: W2A8
-    // 3.6 %, NF4 1.8 %, W8A8 even); on the 128 x 128 W4A8 tile it measured
-    // 4-9 % slower (M = 1024, 2048), so the smaller tiles keep the plain one.
-    // B rows keep the plain one: GRAY measured no faster on any tile.
+    // removes the 16x16x64 loop's bank conflicts (M = N = K = 4096 W4A8 3-6 %
+    // faster) and, on the 32 x 32 loops, measured no slower with the same
+    // (zero) conflicts (W2A8 and NF4 2-4 % faster, W8A8 even); on the
+    // 128 x 128 W4A8 tile it measured 4-5 % slower at M = 1024 in four runs,
+    // so the smaller tiles keep the plain one.  B rows keep the plain one:
+    // GRAY measured no faster on any tile, the ping-pong loop's included.
     static constexpr bool kGrayA = BM == 256 && BN == 256;
     static constexpr int kSA = BM * kBK;                // A bytes per stage
     static constexpr int kSB = BN * kPB;                // B bytes per stage
