@@ -808,9 +808,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_tiled_kernel(
         const int fcol = kM16 ? (lane & 15) : fr;  // the lane's column, fragment-local
         static_assert(kChunksPerRow <= 16 && 16 % kChunksPerRow == 0 && T::kEpiRows % kRowsPerIt == 0,
                       "epilogue copy-out shape");
-        // Copy-out: each 16 lanes read 16 / kChunksPerRow whole rows, spaced by
-        // kRowGap so that, with the 32-byte row padding, their 16-byte chunks
-        // fall in 16 distinct 16-byte bank groups.
+        // Copy-out: each 16 consecutive lanes read 16 / kChunksPerRow whole
+        // rows, spaced by kRowGap so that, with the 32-byte row padding, their
+        // 16-byte chunks fall in 16 distinct 16-byte bank groups.  (The
+        // hardware serves a 16-byte read in other 16-lane groups, see swz(),
+        // under which some groups still meet twice; the copy-out is a few
+        // reads per tile, so that costs nothing measurable.)
         constexpr int kRowsPer16 = 16 / kChunksPerRow;
         constexpr int kRowGap = kRowsPer16 == 4 ? 2 : kRowsPer16 == 2 ? 4 : 1;
         const int q16 = lane >> 4;
