@@ -96,3 +96,35 @@ def test_gelu_dense_sweep(dev, path):
     torch.cuda.synchronize()
     ref = oracle.dequant_act(oracle.gemm_i32(A, Bv), ws, None, "gelu")
     assert_f16_within_1ulp(f16_bits(C), ref, f"gelu sweep {path}")
+
+
+_PP_CACHE = {}
+
+
+@pytest.mark.parametrize("K", [1024, 1088])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu"])
+def test_pingpong_fused_epilogue_full(dev, act, K):
+    """W4A8 at M = N = 4096 runs the 256 x 256 ping-pong kernel; with K =
+    1024 (eight stages) and 1088 (a half stage past the last whole one) the
+    fused epilogue (weight scale, optional per-token scale, activation) is
+    checked on every output after a multi-stage K loop, against the oracle."""
+    from bit_mixed_precision_amd import bq
+    import torch
+
+    M = N = 4096
+    banner(f"pingpong fused act={act} M={M} N={N} K={K}")
+    if K not in _PP_CACHE:
+        g = np.random.default_rng(K)
+        A = synth.int8_uniform(g, (M, K))
+        Bv, Bp, ws = _weights(4, N, K, seed=K + 3)
+        ws = (ws.astype(np.float32) * np.float32(4.0 / np.sqrt(K))).astype(np.float16)
+        xs = synth.fp16_uniform(g, M, 0.25, 1.0)
+        _PP_CACHE.clear()
+        _PP_CACHE[K] = (A, Bp, ws, xs, oracle.gemm_i32(A, Bv))
+    A, Bp, ws, xs, acc = _PP_CACHE[K]
+    Ad, Bd, wsd, xsd = to_dev(A, dev), to_dev(Bp, dev), to_dev(ws, dev), to_dev(xs, dev)
+    C1 = bq.gemm_act(Ad, Bd, 4, wsd, None, act=act)
+    C2 = bq.gemm_act(Ad, Bd, 4, wsd, xsd, act=act)
+    torch.cuda.synchronize()
+    assert_f16_within_1ulp(f16_bits(C1), oracle.dequant_act(acc, ws, None, act), f"pp {act} K={K}")
+    assert_f16_within_1ulp(f16_bits(C2), oracle.dequant_act(acc, ws, xs, act), f"pp {act}+xs K={K}")
